@@ -1,0 +1,173 @@
+/*
+ * migemm.h -- C ABI of a persistent, tile-scheduled, pipelined GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   D = alpha * A * B + beta * C          (fp32 accumulation, bf16 D)
+ *
+ * A is M x K, B is K x N, C and D are M x N.  A and B are both bf16, or both
+ * OCP fp8 e4m3 ("fn": largest finite 448, no infinities); C and D are bf16.
+ *
+ * The operation and its interface shape follow the CUTLASS SM90 "TMA warp-
+ * specialized cooperative" GEMM kernel page: an MNK problem shape, separate
+ * element types and strides for A, B, C and D, an epilogue that forms
+ * alpha * accumulator + beta * C (the source C is loaded only when it is
+ * needed), a feasibility check before launch (can_implement), a caller-owned
+ * workspace with a size query, and a persistent grid sized from the device's
+ * compute-unit count.  The tile hand-off of gemm_run_with_tile_consumer is the
+ * producer acquire/commit and consumer wait/release protocol that CUTLASS
+ * issue #2900 ("How to build a pipeline between epilogue and communication
+ * warp groups?") asks for, so that a consumer stage can work on each finished
+ * output tile while the next tile's main loop runs.
+ *
+ * Conventions shared by every entry point:
+ *   - all sizes and strides are int64_t; strides are in ELEMENTS;
+ *   - element (r, c) of an operand X is at X + r * x_rs + c * x_cs;
+ *   - every device pointer is owned by the caller; the library never
+ *     allocates device memory, never frees, and never synchronizes a stream;
+ *   - a plan owns host memory only and is immutable after creation; one plan
+ *     may be run concurrently on several streams;
+ *   - every call returns a migemm_status (0 = OK, negative = error) and never
+ *     throws.  Argument, device and alignment errors are found before
+ *     anything is launched; a launch failure reported by the HIP runtime gives
+ *     MIGEMM_ERR_LAUNCH; a fault inside a kernel surfaces at the caller's next
+ *     synchronization, as for any HIP kernel.
+ */
+#ifndef MIGEMM_H
+#define MIGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (the pages keep ElementA/B/C/D separate). */
+typedef enum migemm_dtype {
+  MIGEMM_BF16 = 1,
+  MIGEMM_FP8_E4M3 = 2
+} migemm_dtype;
+
+typedef enum migemm_status {
+  MIGEMM_OK = 0,
+  MIGEMM_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, bad stride, C NULL with beta != 0 */
+  MIGEMM_ERR_UNSUPPORTED = -2, /* valid request this library does not implement (see below) */
+  MIGEMM_ERR_MISALIGNED = -3,  /* a base pointer or leading stride is not 16-byte aligned */
+  MIGEMM_ERR_DEVICE = -4,      /* no HIP device, wrong ordinal, or not gfx950 */
+  MIGEMM_ERR_LAUNCH = -5,      /* the HIP runtime rejected the kernel launch */
+  MIGEMM_ERR_TIMEOUT = -6      /* reserved: a bounded device-side wait expired */
+} migemm_status;
+
+/* Plan flags. */
+#define MIGEMM_F_TILE_CONSUMER 0x1u /* plan may run gemm_run_with_tile_consumer */
+
+/* Output tile of the persistent scheduler (and the hand-off unit). */
+#define MIGEMM_TILE_M 256
+#define MIGEMM_TILE_N 256
+
+/*
+ * Problem description (the pages' Arguments: problem shape, element types,
+ * strides, hardware info).
+ *
+ * Layout rules checked by gemm_desc_validate:
+ *   - M, N, K >= 0;
+ *   - type pairs: (A, B, C, D) = (BF16, BF16, BF16, BF16) or
+ *     (FP8_E4M3, FP8_E4M3, BF16, BF16);
+ *   - each of A, B, C, D has exactly one unit stride, and its other stride
+ *     is at least the extent of the contiguous dimension;
+ *   - the non-unit stride times the element size is a multiple of 16 bytes;
+ *   - if A is K-contiguous (a_cs == 1) or B is K-contiguous (b_rs == 1),
+ *     K times the element size is a multiple of 16 bytes;
+ *   - C and D have the same orientation (both row-major or both column-
+ *     major); a column-major D is computed as D^T = B^T A^T;
+ *   - the tile-consumer flag requires a row-major D;
+ *   - the byte span of 256 rows (or K rows) of an operand fits in 2^31.
+ * c_* fields are ignored when the caller will always pass beta == 0, but
+ * must still describe a valid layout (use the same values as D).
+ */
+typedef struct migemm_desc {
+  int64_t M, N, K;
+  int32_t a_type, b_type, c_type, d_type; /* migemm_dtype */
+  int64_t a_rs, a_cs;                     /* A: M x K */
+  int64_t b_rs, b_cs;                     /* B: K x N */
+  int64_t c_rs, c_cs;                     /* C: M x N */
+  int64_t d_rs, d_cs;                     /* D: M x N */
+  int32_t device;                         /* HIP device ordinal; must be gfx950 */
+  uint32_t flags;                         /* MIGEMM_F_* */
+  int32_t max_workgroups;                 /* 0: one persistent workgroup per CU;
+                                             >0: cap on the persistent grid */
+  int32_t reserved;                       /* must be 0 */
+} migemm_desc;
+
+/* What a plan chose (for tracing and tests). */
+typedef struct migemm_plan_info {
+  int64_t tiles_m, tiles_n, num_tiles;
+  int32_t grid;            /* persistent workgroups launched */
+  int32_t block_threads;   /* threads per workgroup (4 waves of 64) */
+  int32_t lds_bytes;       /* LDS per workgroup */
+  int32_t stages;          /* depth of the main-loop LDS ring */
+  int32_t tile_m, tile_n, tile_k;
+  int32_t swapped;         /* 1: column-major D, computed as D^T = B^T A^T */
+  int32_t a_kmajor;        /* 1: A (after any swap) is K-contiguous */
+  int32_t b_kmajor;        /* 1: B (after any swap) is K-contiguous */
+  int32_t cu_count;        /* compute units of the device */
+  int32_t handoff_slots;   /* depth of the tile hand-off ring */
+} migemm_plan_info;
+
+typedef struct migemm_plan migemm_plan; /* opaque, host memory only */
+
+/* Pure host check of a description (the pages' can_implement); needs no
+ * device.  Returns MIGEMM_OK or the error code gemm_plan_create would give
+ * before its device query. */
+int gemm_desc_validate(const migemm_desc* desc);
+
+/* Validate, query the device (must be gfx950), choose the tile configuration
+ * and the persistent grid, and return a plan in *out (set to NULL on error).
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED (strides), DEVICE. */
+int gemm_plan_create(const migemm_desc* desc, migemm_plan** out);
+
+/* Free a plan (NULL is accepted). */
+int gemm_plan_destroy(migemm_plan* plan);
+
+/* Copy the plan's choices into *out. */
+int gemm_plan_get_info(const migemm_plan* plan, migemm_plan_info* out);
+
+/* Bytes of device workspace gemm_run needs (the pages' get_workspace_size).
+ * The static persistent scheduler needs none: 0.  `workspace` arguments
+ * below may then be NULL. */
+size_t gemm_plan_workspace_size(const migemm_plan* plan);
+
+/* D = alpha*A*B + beta*C, enqueued on `stream` (a hipStream_t; NULL = the
+ * null stream).  A, B, D must be non-NULL and 16-byte aligned; C may be NULL
+ * only when beta == 0, in which case C is never read (it may hold NaN).
+ * With K == 0, D = beta*C.  M == 0 or N == 0 is a no-op.  C may alias D only
+ * with identical strides.  Asynchronous: returns once the kernel is queued. */
+int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+             float alpha, float beta, void* workspace, void* stream);
+
+/* gemm_run, and in the same kernel a consumer stage fed through a 2-slot
+ * tile hand-off ring: every finished 256 x 256 tile of D is committed by the
+ * waves that stored it and, while the next tile's main loop runs, consumer
+ * work waits for it, reads it back from D, and then releases the slot.  For
+ * the tile at tile column t = n / 256 it writes, for each row r of the tile,
+ *   row_sum[r * ceil(N/256) + t] = fp32 sum of D[r][256t .. min(N,256t+256)-1]
+ *                                  taken sequentially from +0.0f in ascending
+ *                                  column order over the bf16 values of D,
+ *   row_max[r * ceil(N/256) + t] = IEEE maxNum of the same values from -inf,
+ * and copies the tile bit for bit into D_copy (same strides as D).
+ * row_sum and row_max are M x ceil(N/256) fp32, row-major, 4-byte aligned;
+ * D_copy is 16-byte aligned and must not overlap D.  Requires a plan created
+ * with MIGEMM_F_TILE_CONSUMER and a row-major D. */
+int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const void* B,
+                                const void* C, void* D, float alpha, float beta,
+                                float* row_sum, float* row_max, void* D_copy,
+                                void* workspace, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIGEMM_H */

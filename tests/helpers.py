@@ -1,0 +1,157 @@
+"""Shared test plumbing: run the HIP GEMM through the C ABI on seeded inputs
+and judge the result with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from warp_specialized_pipelined_amd import migemm, synth
+
+BF16, E4M3 = synth.BF16, synth.E4M3
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    """Raw element codes of a CPU or GPU tensor as a flat numpy array."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().reshape(-1)
+    raise TypeError(t.dtype)
+
+
+def oracle_operand(t: torch.Tensor, rs: int, cs: int) -> oracle.Operand:
+    dt = oracle.BF16 if t.dtype == torch.bfloat16 else oracle.E4M3
+    return oracle.Operand(dt, codes(t), rs, cs)
+
+
+def padded_strides(layout, rows, cols, elem_bytes):
+    """(rs, cs, storage shape) with the leading dimension rounded up to 16 bytes."""
+    align = 16 // elem_bytes
+    if layout == "row":
+        ld = max(align, -(-cols // align) * align)
+        return ld, 1, (rows, ld)
+    ld = max(align, -(-rows // align) * align)
+    return 1, ld, (cols, ld)
+
+
+class Problem:
+    """One GEMM problem: CPU storage tensors plus strides, ready for both the
+    GPU path and the oracle.  Storage may be wider than the matrix (padded
+    leading dimension); the padding holds random values the GEMM must ignore."""
+
+    def __init__(self, M, N, K, A, B, C, a_rs, a_cs, b_rs, b_cs, alpha, beta, dtype=BF16,
+                 d_layout="row"):
+        self.M, self.N, self.K = M, N, K
+        self.A, self.B, self.C = A, B, C
+        self.a_rs, self.a_cs, self.b_rs, self.b_cs = a_rs, a_cs, b_rs, b_cs
+        self.alpha, self.beta, self.dtype = alpha, beta, dtype
+        self.d_layout = d_layout
+        self.d_rs, self.d_cs, self.d_shape = padded_strides(d_layout, M, N, 2)
+        self.c_rs, self.c_cs = self.d_rs, self.d_cs
+
+    @classmethod
+    def from_workload(cls, w: synth.Workload):
+        x = synth.make_inputs(w)
+        return cls(w.M, w.N, w.K, x["A"], x["B"], x["C"], x["a_rs"], x["a_cs"], x["b_rs"],
+                   x["b_cs"], x["alpha"], x["beta"], w.dtype)
+
+    @classmethod
+    def random(cls, gen, M, N, K, la="row", lb="row", dtype=BF16, dist="uniform", alpha=1.0,
+               beta=0.0, d_layout="row"):
+        es = 2 if dtype == BF16 else 1
+        a_rs, a_cs, a_shape = padded_strides(la, M, K, es)
+        b_rs, b_cs, b_shape = padded_strides(lb, K, N, es)
+        A = synth.random_matrix(gen, a_shape, dtype, dist, K)
+        B = synth.random_matrix(gen, b_shape, dtype, dist, K)
+        C = None
+        if beta != 0.0:
+            c_shape = padded_strides(d_layout, M, N, 2)[2]
+            C = synth.random_matrix(gen, c_shape, BF16, "normal", K)
+        return cls(M, N, K, A, B, C, a_rs, a_cs, b_rs, b_cs, alpha, beta, dtype, d_layout)
+
+    def desc(self, flags=0, max_workgroups=0, device=0):
+        t = migemm.MIGEMM_BF16 if self.dtype == BF16 else migemm.MIGEMM_FP8_E4M3
+        return migemm.make_desc(self.M, self.N, self.K, t, t, self.a_rs, self.a_cs, self.b_rs,
+                                self.b_cs, self.c_rs, self.c_cs, self.d_rs, self.d_cs, device=device,
+                                flags=flags, max_workgroups=max_workgroups)
+
+    # ---------------------------------------------------------------- GPU
+    def to_device(self, device="cuda"):
+        self.dA = self.A.to(device)
+        self.dB = self.B.to(device)
+        self.dC = self.C.to(device) if self.C is not None else None
+        return self
+
+    def new_d(self, fill=float("nan")):
+        return torch.full(self.d_shape, fill, dtype=torch.bfloat16, device=self.dA.device)
+
+    def run(self, plan, D=None, C_override="keep"):
+        if D is None:
+            D = self.new_d()
+        C = self.dC if C_override == "keep" else C_override
+        migemm.gemm_run(plan.handle, self.dA, self.dB, C, D, self.alpha, self.beta)
+        return D
+
+    # ------------------------------------------------------------- oracle
+    def oracle_ops(self):
+        Aop = oracle_operand(self.A, self.a_rs, self.a_cs)
+        Bop = oracle_operand(self.B, self.b_rs, self.b_cs)
+        Cop = oracle_operand(self.C, self.c_rs, self.c_cs) if self.C is not None else None
+        return Aop, Bop, Cop
+
+    def oracle_full(self, nthreads=0):
+        Aop, Bop, Cop = self.oracle_ops()
+        return oracle.gemm(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta, nthreads)
+
+    def oracle_entries(self, rows, cols, nthreads=0):
+        Aop, Bop, Cop = self.oracle_ops()
+        return oracle.gemm_entries(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta,
+                                   rows, cols, nthreads)
+
+    def d_values(self, D: torch.Tensor) -> np.ndarray:
+        """GPU D (bf16) widened exactly to float64, as a logical M x N array."""
+        v = oracle.bf16_codes_to_f64(codes(D)).reshape(self.d_shape)
+        if self.d_layout == "row":
+            return v[:, :self.N]
+        return v[:, :self.M].T
+
+    def in_dtype(self):
+        return oracle.BF16 if self.dtype == BF16 else oracle.E4M3
+
+
+def check_full(p: Problem, D: torch.Tensor):
+    ref, absum = p.oracle_full()
+    return oracle.check(p.d_values(D), ref, absum, p.in_dtype(), p.alpha)
+
+
+def sample_entries(M, N, n_random=2048, seed=0):
+    """Entries to check at sizes the oracle cannot finish in full: random
+    ones, plus the first/last rows and columns of every 256 x 256 tile edge
+    that falls inside the matrix, plus the four corners."""
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, n_random))
+    cols = list(rng.integers(0, N, n_random))
+    edge_r = sorted({r for t in range(0, M, 256) for r in (t, min(t + 255, M - 1))} | {M - 1})
+    edge_c = sorted({c for t in range(0, N, 256) for c in (t, min(t + 255, N - 1))} | {N - 1})
+    for r in edge_r:
+        cc = rng.integers(0, N, 8)
+        rows += [r] * len(cc)
+        cols += list(cc)
+    for c in edge_c:
+        rr = rng.integers(0, M, 8)
+        rows += list(rr)
+        cols += [c] * len(rr)
+    for r in (0, M - 1):
+        for c in (0, N - 1):
+            rows.append(r)
+            cols.append(c)
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+def check_sampled(p: Problem, D: torch.Tensor, n_random=2048, seed=0):
+    rows, cols = sample_entries(p.M, p.N, n_random, seed)
+    ref, absum = p.oracle_entries(rows, cols)
+    dv = p.d_values(D)[rows, cols]
+    return oracle.check(dv, ref, absum, p.in_dtype(), p.alpha)

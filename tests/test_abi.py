@@ -1,0 +1,159 @@
+"""The C ABI on the host: the library loads, exports what include/migemm.h
+declares with the same struct layout, and rejects bad descriptions with the
+documented status codes before touching a device."""
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from warp_specialized_pipelined_amd import migemm, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "migemm.h")
+
+
+def have_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = migemm.load()
+    names = header_functions()
+    assert names == sorted(migemm.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", migemm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c():
+    prog = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "migemm.h"
+#define F(s, f) printf(#s "." #f " %zu\n", offsetof(s, f))
+int main(void) {
+  printf("sizeof.desc %zu\n", sizeof(migemm_desc));
+  printf("sizeof.info %zu\n", sizeof(migemm_plan_info));
+  F(migemm_desc, M); F(migemm_desc, a_type); F(migemm_desc, a_rs); F(migemm_desc, d_cs);
+  F(migemm_desc, device); F(migemm_desc, flags); F(migemm_desc, max_workgroups);
+  F(migemm_plan_info, grid); F(migemm_plan_info, tile_k); F(migemm_plan_info, handoff_slots);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+    import ctypes
+    assert int(got["sizeof.desc"]) == ctypes.sizeof(migemm.migemm_desc)
+    assert int(got["sizeof.info"]) == ctypes.sizeof(migemm.migemm_plan_info)
+    for key, v in got.items():
+        if key.startswith("sizeof"):
+            continue
+        s, f = key.split(".")
+        cls = migemm.migemm_desc if s == "migemm_desc" else migemm.migemm_plan_info
+        assert getattr(cls, f).offset == int(v), key
+
+
+def desc_for(w: synth.Workload, **over):
+    a_rs, a_cs = synth.strides(w.a_layout, w.M, w.K)
+    b_rs, b_cs = synth.strides(w.b_layout, w.K, w.N)
+    t = migemm.MIGEMM_BF16 if w.dtype == synth.BF16 else migemm.MIGEMM_FP8_E4M3
+    d = dict(M=w.M, N=w.N, K=w.K, a_type=t, b_type=t, a_rs=a_rs, a_cs=a_cs, b_rs=b_rs, b_cs=b_cs,
+             c_rs=w.N, c_cs=1, d_rs=w.N, d_cs=1,
+             flags=migemm.MIGEMM_F_TILE_CONSUMER if w.consumer else 0)
+    d.update(over)
+    return migemm.make_desc(**d)
+
+
+@pytest.mark.parametrize("w", synth.WORKLOADS, ids=lambda w: w.name)
+def test_every_workload_is_a_valid_description(w):
+    assert migemm.gemm_desc_validate(desc_for(w)) == migemm.MIGEMM_OK
+
+
+W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(M=-1), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(K=-5), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(a_type=7), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(a_type=migemm.MIGEMM_FP8_E4M3), migemm.MIGEMM_ERR_UNSUPPORTED),   # mixed A/B types
+    (dict(d_type=migemm.MIGEMM_FP8_E4M3), migemm.MIGEMM_ERR_UNSUPPORTED),
+    (dict(a_rs=4999), migemm.MIGEMM_ERR_INVALID_ARG),                       # stride < extent
+    (dict(a_rs=5000, a_cs=2), migemm.MIGEMM_ERR_INVALID_ARG),               # no unit stride
+    (dict(a_rs=5004), migemm.MIGEMM_ERR_MISALIGNED),                        # 10008-byte rows
+    (dict(b_rs=3004), migemm.MIGEMM_ERR_MISALIGNED),
+    (dict(d_rs=3001), migemm.MIGEMM_ERR_MISALIGNED),
+    (dict(c_rs=1, c_cs=4000), migemm.MIGEMM_ERR_UNSUPPORTED),               # C col, D row
+    (dict(flags=migemm.MIGEMM_F_TILE_CONSUMER, c_rs=1, c_cs=4000, d_rs=1, d_cs=4000),
+     migemm.MIGEMM_ERR_UNSUPPORTED),                                        # consumer needs row D
+    (dict(flags=0x80), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(max_workgroups=-1), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(K=5001, a_rs=5008), migemm.MIGEMM_ERR_MISALIGNED),                # K-contiguous A, K%8
+])
+def test_validation_status_codes(over, status):
+    assert migemm.gemm_desc_validate(desc_for(W, **over)) == status
+
+
+def test_k_contiguity_rule_only_applies_to_k_contiguous_operands():
+    # A column-major (M-contiguous) and B row-major (N-contiguous): any K is fine
+    d = migemm.make_desc(64, 64, 17, 1, 1, 1, 64, 64, 1, 64, 1, 64, 1)
+    assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_OK
+    d = migemm.make_desc(64, 64, 17, 1, 1, 17, 1, 64, 1, 64, 1, 64, 1)      # A row-major
+    assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_ERR_MISALIGNED
+
+
+def test_empty_and_degenerate_shapes_are_valid():
+    for M, N, K in [(0, 0, 0), (0, 16, 16), (16, 0, 16), (16, 16, 0), (1, 1, 8)]:
+        d = migemm.make_desc(M, N, K, 1, 1, max(K, 8), 1, max(N, 8), 1, max(N, 8), 1, max(N, 8), 1)
+        assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_OK, (M, N, K)
+
+
+def test_column_major_d_is_valid():
+    d = migemm.make_desc(100, 60, 64, 1, 1, 64, 1, 60 + 4, 1, 1, 104, 1, 104)
+    assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_OK
+
+
+def test_status_strings():
+    for st in range(-6, 1):
+        s = migemm.gemm_status_string(st)
+        assert s.startswith("MIGEMM_")
+    assert "unknown" in migemm.gemm_status_string(-99)
+
+
+def test_null_arguments_are_rejected_without_a_device():
+    lib = migemm.load()
+    assert lib.gemm_run(None, None, None, None, None, 1.0, 0.0, None, None) == migemm.MIGEMM_ERR_INVALID_ARG
+    assert lib.gemm_plan_create(None, None) == migemm.MIGEMM_ERR_INVALID_ARG
+    assert lib.gemm_plan_get_info(None, None) == migemm.MIGEMM_ERR_INVALID_ARG
+    assert lib.gemm_plan_destroy(None) == migemm.MIGEMM_OK
+    assert migemm.gemm_plan_workspace_size(None) == 0
+
+
+@pytest.mark.skipif(have_gpu(), reason="checks the no-device path")
+def test_plan_create_without_a_gpu_reports_device_error():
+    with pytest.raises(migemm.MigemmError) as e:
+        migemm.gemm_plan_create(desc_for(synth.WORKLOADS[0]))
+    assert e.value.status == migemm.MIGEMM_ERR_DEVICE
+    # validation errors are reported before the device query
+    with pytest.raises(migemm.MigemmError) as e:
+        migemm.gemm_plan_create(desc_for(W, M=-1))
+    assert e.value.status == migemm.MIGEMM_ERR_INVALID_ARG

@@ -1,0 +1,221 @@
+"""Parity of the HIP GEMM with the CPU oracle, element by element, through
+the C ABI (GPU).
+
+Small and mid sizes are checked in full; the five full-size workloads on
+sampled entries (random ones plus every tile-edge row and column).  The bar
+is the per-element acceptance rule held by the oracle package."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from warp_specialized_pipelined_amd import migemm, synth
+from tests.helpers import Problem, check_full, check_sampled, codes
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = list(itertools.product(["row", "col"], ["row", "col"]))
+
+
+def plan_for(p: Problem, **kw):
+    return migemm.Plan(p.desc(**kw))
+
+
+def ok(r):
+    return r["n_fail"] == 0 and r["n_nonfinite"] == 0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- full workloads
+
+@pytest.mark.parametrize("w", synth.WORKLOADS[:3] + synth.WORKLOADS[4:], ids=lambda w: w.name)
+def test_workload(w):
+    print(f"[parity] workload {w.name}", flush=True)
+    p = Problem.from_workload(w).to_device()
+    plan = plan_for(p)
+    D = p.run(plan)
+    torch.cuda.synchronize()
+    if w.M * w.N * w.K <= 256 ** 3:
+        r = check_full(p, D)
+    else:
+        r = check_sampled(p, D, n_random=4096, seed=w.seed)
+    print(r, flush=True)
+    assert ok(r), r
+
+
+def test_workload_8192_plain_gemm():
+    """The 8192^3 bf16 workload through gemm_run (its tile-consumer variant
+    has tests of its own)."""
+    w = synth.WORKLOADS[3]
+    p = Problem.from_workload(w).to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    r = check_sampled(p, D, n_random=4096, seed=w.seed)
+    assert ok(r), r
+
+
+# --------------------------------------------------------------- shape sweep
+
+SHAPES_K_ALIGNED = [(1, 1, 8), (17, 33, 8), (64, 64, 64), (255, 257, 136), (256, 256, 256),
+                    (257, 255, 264), (300, 520, 520), (513, 129, 1000)]
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", SHAPES_K_ALIGNED)
+def test_shapes_bf16(la, lb, M, N, K):
+    g = torch.Generator().manual_seed(M * 7919 + N * 31 + K)
+    p = Problem.random(g, M, N, K, la, lb, dist="normal").to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    r = check_full(p, D)
+    assert ok(r), (la, lb, M, N, K, r)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (15, 17, 17), (100, 300, 255), (257, 129, 63)])
+def test_shapes_any_k_mn_contiguous(M, N, K):
+    """A column-major and B row-major: K needs no alignment."""
+    g = torch.Generator().manual_seed(K)
+    p = Problem.random(g, M, N, K, "col", "row", dist="normal").to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    assert ok(check_full(p, D))
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (257, 300, 192), (128, 384, 1040)])
+def test_shapes_fp8(la, lb, M, N, K):
+    g = torch.Generator().manual_seed(M + N + K)
+    p = Problem.random(g, M, N, K, la, lb, dtype=synth.E4M3, alpha=0.0625).to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    r = check_full(p, D)
+    assert ok(r), (la, lb, M, N, K, r)
+
+
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.5), (-0.5, 1.0), (0.125, -2.0), (0.0, 1.0)])
+def test_alpha_beta(alpha, beta):
+    g = torch.Generator().manual_seed(99)
+    p = Problem.random(g, 300, 280, 264, "row", "col", dist="normal", alpha=alpha, beta=beta)
+    p.to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    assert ok(check_full(p, D))
+
+
+def test_column_major_d_and_c():
+    g = torch.Generator().manual_seed(5)
+    p = Problem.random(g, 300, 200, 136, "row", "row", dist="normal", alpha=1.0, beta=0.75,
+                       d_layout="col").to_device()
+    plan = plan_for(p)
+    assert plan.info.swapped == 1
+    D = p.run(plan)
+    torch.cuda.synchronize()
+    assert ok(check_full(p, D))
+
+
+# ------------------------------------------------------ semantics and edges
+
+def test_beta_zero_ignores_c_even_nan():
+    g = torch.Generator().manual_seed(6)
+    p = Problem.random(g, 256, 256, 128, dist="normal").to_device()
+    plan = plan_for(p)
+    D1 = p.run(plan, C_override=None)
+    nanC = torch.full((256, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    D2 = p.run(plan, C_override=nanC)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+    assert ok(check_full(p, D1))
+
+
+def test_k_zero_gives_beta_c():
+    g = torch.Generator().manual_seed(1)
+    p = Problem.random(g, 260, 130, 0, "row", "row", alpha=1.0, beta=2.0).to_device()
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    assert ok(check_full(p, D))
+    want = (2.0 * p.C[:, :130].to(torch.float32)).to(torch.bfloat16)   # doubling is exact
+    assert torch.equal(D.cpu()[:, :130].view(torch.int16), want.view(torch.int16))
+
+
+def test_empty_output_is_a_no_op():
+    for M, N in [(0, 64), (64, 0)]:
+        desc = migemm.make_desc(M, N, 64, 1, 1, 64, 1, max(N, 8), 1, max(N, 8), 1, max(N, 8), 1)
+        plan = migemm.Plan(desc)
+        assert migemm.gemm_run(plan.handle, 0, 0, 0, 0, 1.0, 0.0) == migemm.MIGEMM_OK
+
+
+def test_exact_small_integer_results():
+    """All-ones gives K exactly; A = I gives B bit for bit; entries in
+    {-1, 0, 1} with K <= 256 give exact integers."""
+    K = 4096
+    A = torch.ones((256, K), dtype=torch.bfloat16, device="cuda")
+    B = torch.ones((K, 256), dtype=torch.bfloat16, device="cuda")
+    D = torch.empty((256, 256), dtype=torch.bfloat16, device="cuda")
+    plan = migemm.Plan(migemm.make_desc(256, 256, K, 1, 1, K, 1, 256, 1, 256, 1, 256, 1))
+    migemm.gemm_run(plan.handle, A, B, None, D, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.all(D.float() == K)
+
+    g = torch.Generator().manual_seed(3)
+    Bm = torch.randn((512, 384), generator=g).to(torch.bfloat16)
+    I = torch.eye(512, dtype=torch.bfloat16)
+    D = torch.empty((512, 384), dtype=torch.bfloat16, device="cuda")
+    plan = migemm.Plan(migemm.make_desc(512, 384, 512, 1, 1, 512, 1, 384, 1, 384, 1, 384, 1))
+    migemm.gemm_run(plan.handle, I.cuda(), Bm.cuda(), None, D, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(D.cpu().view(torch.int16), Bm.view(torch.int16))
+
+    Ai = synth.small_int_matrix(g, (300, 256))
+    Bi = synth.small_int_matrix(g, (256, 200))
+    exact = Ai.to(torch.float64) @ Bi.to(torch.float64)
+    D = torch.empty((300, 200), dtype=torch.bfloat16, device="cuda")
+    plan = migemm.Plan(migemm.make_desc(300, 200, 256, 1, 1, 256, 1, 200, 1, 200, 1, 200, 1))
+    migemm.gemm_run(plan.handle, Ai.cuda(), Bi.cuda(), None, D, 1.0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(D.cpu().to(torch.float64), exact)
+
+
+def test_deterministic_across_runs_and_grid_sizes():
+    g = torch.Generator().manual_seed(12)
+    p = Problem.random(g, 1000, 1200, 520, "row", "row", dist="normal").to_device()
+    outs = []
+    for mw in (0, 0, 7, 64):
+        outs.append(p.run(plan_for(p, max_workgroups=mw)))
+    torch.cuda.synchronize()
+    for D in outs[1:]:
+        assert torch.equal(D.view(torch.int16), outs[0].view(torch.int16))
+    assert ok(check_full(p, outs[0]))
+
+
+def test_plan_info_matches_the_persistent_design():
+    g = torch.Generator().manual_seed(1)
+    p = Problem.random(g, 4000, 3000, 64)
+    info = migemm.Plan(p.desc()).info
+    assert (info.tiles_m, info.tiles_n, info.num_tiles) == (16, 12, 192)
+    assert info.grid == min(192, info.cu_count)
+    assert info.block_threads == 256 and info.tile_m == 256 and info.tile_n == 256
+    assert info.lds_bytes <= 160 * 1024
+    props = torch.cuda.get_device_properties(0)
+    assert info.cu_count == props.multi_processor_count
+    assert "gfx950" in props.gcnArchName
+
+
+def test_misaligned_pointer_is_rejected_before_launch():
+    g = torch.Generator().manual_seed(2)
+    p = Problem.random(g, 64, 64, 64).to_device()
+    plan = plan_for(p)
+    D = p.new_d()
+    base = torch.empty(64 * 64 + 8, dtype=torch.bfloat16, device="cuda")
+    st = migemm.gemm_run(plan.handle, base[1:].data_ptr(), p.dB, None, D, 1.0, 0.0, check=False)
+    assert st == migemm.MIGEMM_ERR_MISALIGNED
+    st = migemm.gemm_run(plan.handle, p.dA, p.dB, None, D, 1.0, 0.5, check=False)
+    assert st == migemm.MIGEMM_ERR_INVALID_ARG   # beta != 0 needs C

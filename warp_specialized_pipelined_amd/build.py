@@ -1,0 +1,65 @@
+"""Build libmigemm.so in-tree with hipcc for gfx950.
+
+    python -m warp_specialized_pipelined_amd.build          # build
+    python -m warp_specialized_pipelined_amd.build --asm    # also dump AMD assembly
+
+The library is written next to this file so that it travels with the source
+tree; nothing is installed.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmigemm.so")
+ARCH = "gfx950"
+
+SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "gemm_kernels.hip")]
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    # keep the compiler from forming packed fp32 arithmetic instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"), "hipcc"):
+        if os.path.sep not in cand or os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libmigemm.so (always recompiles)."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=CSRC)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def dump_asm(out_dir: str) -> str:
+    """Write the gfx950 assembly of the kernel translation unit to out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "gemm_kernels.s")
+    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", "-o", out,
+           os.path.join(CSRC, "gemm_kernels.hip")]
+    subprocess.run(cmd, check=True, cwd=CSRC)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    if "--asm" in sys.argv:
+        print(dump_asm(os.path.join(os.path.dirname(HERE), "_work", "asm")))

@@ -1,0 +1,307 @@
+// api.cpp -- the C ABI: description checks (the pages' can_implement), plan
+// creation (device query, tile configuration, persistent grid size) and the
+// run entry points.  See include/migemm.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/migemm.h"
+#include "kernel/params.hpp"
+#include "launch.h"
+
+using migemm::KernelArgs;
+using migemm::KernelSelect;
+
+struct migemm_plan {
+  migemm_desc desc;
+  KernelSelect sel;
+  KernelArgs base;   // shape/stride part of the kernel arguments
+  int64_t M, N, K;   // problem after any swap (D row-major)
+  bool swapped;
+  int grid;
+  int cu_count;
+  int device;
+};
+
+namespace {
+
+// Orientation of one operand: K-contiguous ("row" for A, "col" for B) or not,
+// and its leading (non-unit) stride.
+struct Orient {
+  bool row_major;  // column stride is 1
+  int64_t ld;      // the non-unit stride
+};
+
+// rows x cols matrix with strides (rs, cs): exactly one unit stride, and the
+// other at least the contiguous extent.  Row-major wins when both are 1.
+bool orient(int64_t rows, int64_t cols, int64_t rs, int64_t cs, Orient* o) {
+  if (cs == 1 && rs >= (cols > 1 ? cols : 1)) {
+    *o = {true, rs};
+    return true;
+  }
+  if (rs == 1 && cs >= (rows > 1 ? rows : 1)) {
+    *o = {false, cs};
+    return true;
+  }
+  return false;
+}
+
+int64_t extent_bytes(int64_t rows, int64_t cols, int64_t rs, int64_t cs, int es) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((rows - 1) * rs + (cols - 1) * cs + 1) * es;
+}
+
+int elem_size(int32_t t) { return t == MIGEMM_BF16 ? 2 : (t == MIGEMM_FP8_E4M3 ? 1 : 0); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxRsrcSpan = 0x7FFFFFF0 - 1024;
+
+// Everything after any swap: the canonical problem the kernel sees.
+struct Canon {
+  int64_t M, N, K;
+  int64_t a_rs, a_cs, b_rs, b_cs, c_rs, c_cs, d_rs, d_cs;
+  bool swapped;
+};
+
+int validate(const migemm_desc* d, Canon* out) {
+  if (!d) return MIGEMM_ERR_INVALID_ARG;
+  if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0)
+    return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & ~MIGEMM_F_TILE_CONSUMER) != 0) return MIGEMM_ERR_INVALID_ARG;
+  const int es = elem_size(d->a_type);
+  if (es == 0 || elem_size(d->b_type) == 0 || elem_size(d->c_type) == 0 ||
+      elem_size(d->d_type) == 0)
+    return MIGEMM_ERR_INVALID_ARG;
+  if (d->a_type != d->b_type || d->c_type != MIGEMM_BF16 || d->d_type != MIGEMM_BF16)
+    return MIGEMM_ERR_UNSUPPORTED;
+  Orient oa, ob, oc, od;
+  if (!orient(d->M, d->K, d->a_rs, d->a_cs, &oa) || !orient(d->K, d->N, d->b_rs, d->b_cs, &ob) ||
+      !orient(d->M, d->N, d->c_rs, d->c_cs, &oc) || !orient(d->M, d->N, d->d_rs, d->d_cs, &od))
+    return MIGEMM_ERR_INVALID_ARG;
+  if (oc.row_major != od.row_major) return MIGEMM_ERR_UNSUPPORTED;
+  if ((d->flags & MIGEMM_F_TILE_CONSUMER) && !od.row_major) return MIGEMM_ERR_UNSUPPORTED;
+  // 16-byte rows for every operand.
+  if ((oa.ld * es) % 16 || (ob.ld * es) % 16 || (oc.ld * 2) % 16 || (od.ld * 2) % 16)
+    return MIGEMM_ERR_MISALIGNED;
+  // A K-contiguous operand is fetched in 16-byte chunks along K.
+  const bool a_k = oa.row_major, b_k = !ob.row_major;
+  if ((a_k || b_k) && (d->K * es) % 16) return MIGEMM_ERR_MISALIGNED;
+
+  Canon c;
+  if (od.row_major) {
+    c = {d->M, d->N, d->K, d->a_rs, d->a_cs, d->b_rs, d->b_cs,
+         d->c_rs, d->c_cs, d->d_rs, d->d_cs, false};
+  } else {
+    // D^T = B^T A^T: swap the roles of A and B and transpose every operand.
+    c = {d->N, d->M, d->K, d->b_cs, d->b_rs, d->a_cs, d->a_rs,
+         d->c_cs, d->c_rs, d->d_cs, d->d_rs, true};
+  }
+  // 32-bit buffer offsets: 256 rows of a K-contiguous operand, or one stage
+  // of K rows of an MN-contiguous one, must span less than 2^31 bytes.
+  const int64_t bk = migemm::kStageKBytes / es;
+  Orient ca, cb;
+  orient(c.M, c.K, c.a_rs, c.a_cs, &ca);
+  orient(c.K, c.N, c.b_rs, c.b_cs, &cb);
+  const bool ca_k = ca.row_major, cb_k = !cb.row_major;
+  const int64_t span_a = (ca_k ? migemm::kTileM : bk) * ca.ld * es;
+  const int64_t span_b = (cb_k ? migemm::kTileN : bk) * cb.ld * es;
+  if (span_a > kMaxRsrcSpan || span_b > kMaxRsrcSpan) return MIGEMM_ERR_UNSUPPORTED;
+  // The epilogue addresses a 256-row band of C and D with 32-bit offsets too.
+  if ((int64_t)migemm::kTileM * c.c_rs * 2 > kMaxRsrcSpan ||
+      (int64_t)migemm::kTileM * c.d_rs * 2 > kMaxRsrcSpan)
+    return MIGEMM_ERR_UNSUPPORTED;
+  if (c.M / migemm::kTileM >= (1 << 20) || c.N / migemm::kTileN >= (1 << 20))
+    return MIGEMM_ERR_UNSUPPORTED;
+  if (out) *out = c;
+  return MIGEMM_OK;
+}
+
+bool trace_enabled() {
+  const char* e = std::getenv("MIGEMM_TRACE");
+  return e && e[0] && e[0] != '0';
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_desc_validate(const migemm_desc* desc) { return validate(desc, nullptr); }
+
+int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
+  if (!out) return MIGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  Canon c;
+  int st = validate(desc, &c);
+  if (st != MIGEMM_OK) return st;
+
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return MIGEMM_ERR_DEVICE;
+  if (desc->device < 0 || desc->device >= count) return MIGEMM_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, desc->device) != hipSuccess) return MIGEMM_ERR_DEVICE;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MIGEMM_ERR_DEVICE;
+  if (prop.sharedMemPerBlock < (size_t)migemm::kLdsBytes) return MIGEMM_ERR_DEVICE;
+
+  migemm_plan* p = new (std::nothrow) migemm_plan;
+  if (!p) return MIGEMM_ERR_INVALID_ARG;
+  std::memset(p, 0, sizeof(*p));
+  p->desc = *desc;
+  p->device = desc->device;
+  p->cu_count = prop.multiProcessorCount;
+  p->M = c.M;
+  p->N = c.N;
+  p->K = c.K;
+  p->swapped = c.swapped;
+
+  const int es = elem_size(desc->a_type);
+  Orient oa, ob;
+  orient(c.M, c.K, c.a_rs, c.a_cs, &oa);
+  orient(c.K, c.N, c.b_rs, c.b_cs, &ob);
+  p->sel.elem_bytes = es;
+  p->sel.a_kmajor = oa.row_major;   // A row-major = K-contiguous
+  p->sel.b_kmajor = !ob.row_major;  // B column-major = K-contiguous
+  p->sel.consumer = false;
+
+  KernelArgs& a = p->base;
+  a.M = c.M;
+  a.N = c.N;
+  a.K = c.K;
+  a.lda = oa.ld;
+  a.ldb = ob.ld;
+  a.ldc = c.c_rs;
+  a.ldd = c.d_rs;
+  a.a_bytes = extent_bytes(c.M, c.K, c.a_rs, c.a_cs, es);
+  a.b_bytes = extent_bytes(c.K, c.N, c.b_rs, c.b_cs, es);
+  a.tiles_m = (int32_t)((c.M + migemm::kTileM - 1) / migemm::kTileM);
+  a.tiles_n = (int32_t)((c.N + migemm::kTileN - 1) / migemm::kTileN);
+  a.num_tiles = a.tiles_m * a.tiles_n;
+  a.group_m = a.tiles_m < 8 ? (a.tiles_m > 0 ? a.tiles_m : 1) : 8;
+  a.stat_ld = a.tiles_n;
+
+  int grid = p->cu_count;
+  if (desc->max_workgroups > 0 && desc->max_workgroups < grid) grid = desc->max_workgroups;
+  if (a.num_tiles < grid) grid = a.num_tiles;
+  p->grid = grid;
+
+  hipError_t e = migemm::prepare_kernel(p->sel);
+  if (e == hipSuccess && (desc->flags & MIGEMM_F_TILE_CONSUMER)) {
+    KernelSelect s = p->sel;
+    s.consumer = true;
+    e = migemm::prepare_kernel(s);
+  }
+  if (e != hipSuccess) {
+    delete p;
+    return MIGEMM_ERR_DEVICE;
+  }
+  if (trace_enabled()) {
+    std::fprintf(stderr,
+                 "[migemm] plan M=%lld N=%lld K=%lld es=%d A:%s B:%s swapped=%d tiles=%dx%d "
+                 "grid=%d group_m=%d lds=%d stages=%d cus=%d\n",
+                 (long long)c.M, (long long)c.N, (long long)c.K, es,
+                 p->sel.a_kmajor ? "K-contig" : "M-contig", p->sel.b_kmajor ? "K-contig" : "N-contig",
+                 (int)c.swapped, a.tiles_m, a.tiles_n, grid, a.group_m, migemm::kLdsBytes,
+                 migemm::kStages, p->cu_count);
+  }
+  *out = p;
+  return MIGEMM_OK;
+}
+
+int gemm_plan_destroy(migemm_plan* plan) {
+  delete plan;
+  return MIGEMM_OK;
+}
+
+int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
+  if (!p || !out) return MIGEMM_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->tiles_m = p->base.tiles_m;
+  out->tiles_n = p->base.tiles_n;
+  out->num_tiles = p->base.num_tiles;
+  out->grid = p->grid;
+  out->block_threads = migemm::kThreads;
+  out->lds_bytes = migemm::kLdsBytes;
+  out->stages = migemm::kStages;
+  out->tile_m = migemm::kTileM;
+  out->tile_n = migemm::kTileN;
+  out->tile_k = migemm::kStageKBytes / p->sel.elem_bytes;
+  out->swapped = p->swapped ? 1 : 0;
+  out->a_kmajor = p->sel.a_kmajor ? 1 : 0;
+  out->b_kmajor = p->sel.b_kmajor ? 1 : 0;
+  out->cu_count = p->cu_count;
+  out->handoff_slots = migemm::kHandoffSlots;
+  return MIGEMM_OK;
+}
+
+size_t gemm_plan_workspace_size(const migemm_plan* plan) {
+  (void)plan;
+  return 0;
+}
+
+static int run_common(const migemm_plan* p, const void* A, const void* B, const void* C, void* D,
+                      float alpha, float beta, bool consumer, float* row_sum, float* row_max,
+                      void* D_copy, void* stream) {
+  if (!p) return MIGEMM_ERR_INVALID_ARG;
+  if (consumer && !(p->desc.flags & MIGEMM_F_TILE_CONSUMER)) return MIGEMM_ERR_INVALID_ARG;
+  if (p->M == 0 || p->N == 0) return MIGEMM_OK;
+  if (!D || (p->K > 0 && (!A || !B))) return MIGEMM_ERR_INVALID_ARG;
+  if (beta != 0.0f && !C) return MIGEMM_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(D) || (beta != 0.0f && !aligned16(C)))
+    return MIGEMM_ERR_MISALIGNED;
+  if (consumer) {
+    if (!row_sum || !row_max || !D_copy) return MIGEMM_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(row_sum) & 3u) || (reinterpret_cast<uintptr_t>(row_max) & 3u) ||
+        !aligned16(D_copy))
+      return MIGEMM_ERR_MISALIGNED;
+    if (!(p->base.tiles_n > 0)) return MIGEMM_ERR_INVALID_ARG;
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return MIGEMM_ERR_DEVICE;
+
+  KernelArgs a = p->base;
+  // After a swap (column-major D) A and B trade places.
+  a.A = p->swapped ? B : A;
+  a.B = p->swapped ? A : B;
+  a.C = beta != 0.0f ? C : nullptr;
+  a.D = D;
+  a.row_sum = row_sum;
+  a.row_max = row_max;
+  a.D_copy = D_copy;
+  a.alpha = alpha;
+  a.beta = beta;
+  KernelSelect s = p->sel;
+  s.consumer = consumer;
+  hipError_t e = migemm::launch_gemm(s, a, p->grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIGEMM_OK : MIGEMM_ERR_LAUNCH;
+}
+
+int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+             float alpha, float beta, void* workspace, void* stream) {
+  (void)workspace;
+  return run_common(plan, A, B, C, D, alpha, beta, false, nullptr, nullptr, nullptr, stream);
+}
+
+int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const void* B,
+                                const void* C, void* D, float alpha, float beta, float* row_sum,
+                                float* row_max, void* D_copy, void* workspace, void* stream) {
+  (void)workspace;
+  return run_common(plan, A, B, C, D, alpha, beta, true, row_sum, row_max, D_copy, stream);
+}
+
+const char* gemm_status_string(int status) {
+  switch (status) {
+    case MIGEMM_OK: return "MIGEMM_OK";
+    case MIGEMM_ERR_INVALID_ARG: return "MIGEMM_ERR_INVALID_ARG: invalid argument";
+    case MIGEMM_ERR_UNSUPPORTED: return "MIGEMM_ERR_UNSUPPORTED: valid request not implemented";
+    case MIGEMM_ERR_MISALIGNED: return "MIGEMM_ERR_MISALIGNED: pointer or stride not 16-byte aligned";
+    case MIGEMM_ERR_DEVICE: return "MIGEMM_ERR_DEVICE: no usable gfx950 device";
+    case MIGEMM_ERR_LAUNCH: return "MIGEMM_ERR_LAUNCH: kernel launch failed";
+    case MIGEMM_ERR_TIMEOUT: return "MIGEMM_ERR_TIMEOUT: device wait timed out";
+    default: return "unknown migemm status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// epilogue.hpp -- D = alpha * acc + beta * C in fp32, rounded to bf16
+// (nearest even), staged through LDS and stored to a row-major D with
+// 16-byte stores.
+//
+// The pages' epilogue copies accumulators to registers, converts them to the
+// output type, writes them to a shared-memory staging buffer, synchronizes,
+// and then copies whole rows of the staged tile out to global memory; it
+// reads the source C only when the epilogue needs it (CuTe DSL persistent GEMM
+// epilogue quoted in CUTLASS issue #2900; kernel page: is_producer_load_needed
+// and collective_epilogue.store).
+//
+// Here each wave stages its own 128 x 128 quarter of the tile as bf16 in a
+// slice of the (now idle) main-loop ring:
+//   - with the (B^T A^T) block orientation of the main loop a lane holds four
+//     consecutive columns of one row per group of four accumulators, so the
+//     staging writes are 8-byte ds_write_b64 (lanes l and l+32 fill one
+//     16-byte chunk of a row);
+//   - staged rows are padded to 272 bytes, which puts consecutive rows 4 banks
+//     apart: the 32 rows one write touches and the 4 rows one read touches
+//     spread over all banks, and every address is a per-lane base plus a
+//     constant, so it folds into the instruction's offset field;
+//   - read back, one ds_read_b128 per lane covers 4 full 256-byte rows, which
+//     leave as coalesced 16-byte buffer stores.
+// C (when beta != 0) is read in the accumulator layout, 8 bytes per lane, so
+// that alpha*acc + beta*C is formed in fp32 and rounded once.
+#pragma once
+
+#include "gfx950.hpp"
+#include "mainloop.hpp"
+#include "params.hpp"
+
+namespace migemm {
+
+// A buffer resource over a row-major bf16 matrix, starting at (r0, c0).
+// round16: extend the range to the end of the last 16-byte block (for reads;
+// range checks work per dword, see OperandLoader::issue).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t matrix_rsrc(const void* base, int64_t ld,
+                                                              int64_t rows, int64_t cols,
+                                                              int64_t r0, int64_t c0, bool round16) {
+  const unsigned short* p = static_cast<const unsigned short*>(base) + r0 * ld + c0;
+  int64_t bytes = (r0 < rows && c0 < cols) ? ((rows - 1 - r0) * ld + (cols - c0)) * 2 : 0;
+  if (round16) bytes = (bytes + 15) & ~(int64_t)15;
+  bytes = bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes;
+  return make_rsrc(p, (uint32_t)bytes);
+}
+
+// Stage, then store.  The ring must be idle (all waves past the main loop's
+// closing barrier).  Returns with this wave's global stores issued.
+__device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArgs& a, int tm, int tn,
+                                               int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)tm * kTileM + wm * kWaveTile;   // first row of the wave tile
+  const int64_t n0 = (int64_t)tn * kTileN + wn * kWaveTile;   // first column
+  const int lr = lane & 31;            // row within a 32 x 32 block
+  const int half = lane >> 5;          // which 4 of the 8 columns of a chunk
+  const uint32_t st_base = wave * kStagingWaveBytes + lr * kStagingRowBytes + 8 * half;
+
+  if (a.beta != 0.0f) {
+    const __amdgpu_buffer_rsrc_t rc = matrix_rsrc(a.C, a.ldc, a.M, a.N, m0, n0, true);
+    const uint32_t c_lane = (uint32_t)((lr * a.ldc + 4 * half) * 2);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const uint32_t c_row = c_lane + (uint32_t)(32 * bi * a.ldc * 2);
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // Out-of-range C reads return 0 or land in columns >= N; either way
+          // they only feed outputs that are never stored.
+          const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(rc, c_row + (32 * bj + 8 * q) * 2, 0, 0);
+          const f32x16& r = acc.v[bi][bj];
+          const float v0 = a.alpha * r[4 * q + 0] + a.beta * bf16_lo(cw[0]);
+          const float v1 = a.alpha * r[4 * q + 1] + a.beta * bf16_hi(cw[0]);
+          const float v2 = a.alpha * r[4 * q + 2] + a.beta * bf16_lo(cw[1]);
+          const float v3 = a.alpha * r[4 * q + 3] + a.beta * bf16_hi(cw[1]);
+          const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          *(MIGEMM_LDS u32x2*)lds_at(st_base + 32 * bi * kStagingRowBytes + (4 * bj + q) * 16) = w;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& r = acc.v[bi][bj];
+          const u32x2 w = {pack_bf16x2(a.alpha * r[4 * q + 0], a.alpha * r[4 * q + 1]),
+                           pack_bf16x2(a.alpha * r[4 * q + 2], a.alpha * r[4 * q + 3])};
+          *(MIGEMM_LDS u32x2*)lds_at(st_base + 32 * bi * kStagingRowBytes + (4 * bj + q) * 16) = w;
+        }
+  }
+
+  // The wave reads back only what it wrote itself: LDS accesses of one wave
+  // complete in order, so no barrier is needed here.
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(a.D, a.ldd, a.M, a.N, m0, n0, false);
+  const int rsub = lane >> 4;          // 4 rows per read
+  const int chunk = lane & 15;
+  const int64_t rows_left = a.M - m0;
+  const int64_t cols_left = a.N - n0 - 8 * chunk;   // valid columns from this lane's chunk on
+  const uint32_t rd_base = wave * kStagingWaveBytes + rsub * kStagingRowBytes + chunk * 16;
+  const uint32_t d_lane = (uint32_t)((rsub * a.ldd + 8 * chunk) * 2);
+#pragma unroll 8
+  for (int i = 0; i < kWaveTile / 4; ++i) {
+    const u32x4 v = *(const MIGEMM_LDS u32x4*)lds_at(rd_base + 4 * i * kStagingRowBytes);
+    const int row = 4 * i + rsub;
+    if (row < rows_left && cols_left > 0) {
+      const uint32_t off = d_lane + (uint32_t)(4 * i * a.ldd * 2);
+      if (cols_left >= 8) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+      } else {
+        for (int e = 0; e < cols_left; ++e)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), rd,
+                                                off + 2 * e, 0, 0);
+      }
+    }
+  }
+}
+
+}  // namespace migemm

@@ -1,0 +1,55 @@
+// params.hpp -- the argument block every GEMM kernel receives, and the
+// compile-time tile geometry.  Shared by host and device code.
+#pragma once
+
+#include <stdint.h>
+
+namespace migemm {
+
+// Output tile 256 x 256, 4 waves per workgroup as a 2 x 2 grid of 128 x 128
+// wave tiles, one persistent workgroup per compute unit.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveTile = 128;
+// Each main-loop stage holds 64 bytes of K for every row of the A and B
+// tiles (32 bf16 or 64 e4m3 values): 16 KiB of A + 16 KiB of B.
+constexpr int kStageKBytes = 64;
+constexpr int kOperandStageBytes = kTileM * kStageKBytes;  // 16 KiB
+constexpr int kStageBytes = 2 * kOperandStageBytes;        // 32 KiB
+constexpr int kStages = 4;                                 // LDS ring depth
+constexpr int kRingBytes = kStages * kStageBytes;          // 128 KiB
+// Epilogue staging: each wave's 128 x 128 bf16 quarter of the tile, rows
+// padded from 256 to 272 bytes so that consecutive rows start 4 banks apart.
+// It overlays the (then idle) ring and runs a little past it.
+constexpr int kStagingRowBytes = kWaveTile * 2 + 16;                 // 272
+constexpr int kStagingWaveBytes = kWaveTile * kStagingRowBytes;      // 34816
+constexpr int kStagingBytes = kWaves * kStagingWaveBytes;            // 139264
+// Tile hand-off ring: two slots of {tile id, full count, empty count}.
+constexpr int kHandoffSlots = 2;
+constexpr int kHandoffOffset = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
+constexpr int kHandoffBytes = 64;
+constexpr int kLdsBytes = kHandoffOffset + kHandoffBytes;
+
+struct KernelArgs {
+  const void* A;       // operand storage (after any swap of A and B)
+  const void* B;
+  const void* C;       // NULL when beta == 0
+  void* D;
+  float* row_sum;      // consumer outputs (tile-consumer kernels only)
+  float* row_max;
+  void* D_copy;
+  int64_t M, N, K;
+  int64_t lda, ldb;    // the non-unit stride of A and B, in elements
+  int64_t ldc, ldd;    // row strides of C and D (row-major after any swap)
+  int64_t a_bytes;     // byte extent of A and B as described by the strides
+  int64_t b_bytes;
+  float alpha, beta;
+  int32_t tiles_m, tiles_n, num_tiles;
+  int32_t group_m;     // tile rows per raster group
+  int32_t stat_ld;     // ceil(N / 256): leading dimension of row_sum/row_max
+  int32_t pad;
+};
+
+}  // namespace migemm

@@ -1,0 +1,24 @@
+// launch.h -- internal interface between the host plan layer (api.cpp) and
+// the kernel translation unit (gemm_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernel/params.hpp"
+
+namespace migemm {
+
+struct KernelSelect {
+  int elem_bytes;   // 2: bf16 operands, 1: e4m3 operands
+  bool a_kmajor;    // A is K-contiguous
+  bool b_kmajor;    // B is K-contiguous
+  bool consumer;    // tile hand-off + consumer stage
+};
+
+// Raise the kernel's dynamic-LDS limit to what it uses (once per process).
+hipError_t prepare_kernel(const KernelSelect& sel);
+
+// Enqueue one persistent GEMM kernel on `stream` with `grid` workgroups.
+hipError_t launch_gemm(const KernelSelect& sel, const KernelArgs& args, int grid, hipStream_t stream);
+
+}  // namespace migemm
