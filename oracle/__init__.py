@@ -32,6 +32,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation test points this at deliberately broken builds of oracle.c to
+# check that the pins catch them.
+_LIB_OVERRIDE = os.environ.get("MIGEMM_ORACLE_LIB")
 
 BF16 = 1
 E4M3 = 2
@@ -58,9 +61,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_value.restype = dbl

@@ -15,6 +15,19 @@
 
 namespace migemm {
 
+// The lane and wave index as values the compiler cannot see through.  Every
+// per-lane offset of the K loop and the epilogue derives from them; taking
+// them afresh for each tile keeps those offsets from being computed once
+// before the tile loop and held (or spilled) across the whole of it -- a
+// spilled offset comes back with a vmcnt(0) that would drain the ring.
+struct LaneIds {
+  int lane, wave;
+  __device__ __forceinline__ LaneIds(int l, int w) : lane(l), wave(w) {
+    asm volatile("" : "+v"(lane));
+    asm volatile("" : "+s"(wave));
+  }
+};
+
 template <int ES, bool AK, bool BK, bool CONS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
   const int lane = threadIdx.x & 63;
@@ -25,8 +38,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     NoSideWork none;
     for (int L = first; L < a.num_tiles; L += gridDim.x) {
       const TileCoord t = tile_of(L, a);
-      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, wave, lane, none);
-      epilogue_store(acc, a, t.tm, t.tn, wave, lane);
+      const LaneIds id(lane, wave);
+      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none);
+      const LaneIds ie(lane, wave);
+      epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
       wait_lgkmcnt<0>();  // staging reads done ...
       barrier();          // ... in every wave before the ring is refilled
     }
@@ -42,18 +57,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
       const TileCoord t = tile_of(L, a);
       if (n > 0) cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
-      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, wave, lane, cons);
-      cons.drain(lane);
+      const LaneIds id(lane, wave);
+      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, cons);
+      cons.drain(a, wave, lane);
       const int s = n % kHandoffSlots;
       HandoffRing::acquire(s, n / kHandoffSlots);
-      epilogue_store(acc, a, t.tm, t.tn, wave, lane);
+      const LaneIds ie(lane, wave);
+      epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
       HandoffRing::commit(s, L, wave, lane);
       wait_lgkmcnt<0>();
       barrier();
     }
     if (n > 0) {
       cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
-      cons.drain(lane);
+      cons.drain(a, wave, lane);
     }
   }
 }

@@ -74,9 +74,9 @@ struct HandoffRing {
     return (int)__atomic_load_n(word(slot, kTileId), __ATOMIC_RELAXED);
   }
   // The slot (its tile id) is free again.  The consumer's reads of the tile
-  // have completed by then: its last fetched chunk was folded in just before,
-  // and vector loads complete in order.  The payload in D is never
-  // overwritten inside one kernel, so no memory fence is needed.
+  // have completed by then (its last fetch was waited for and read back just
+  // before), and the payload in D is never overwritten inside one kernel, so
+  // no memory fence is needed.
   __device__ __forceinline__ static void release(int slot, int lane) {
     compiler_fence();
     if (lane == 0) __atomic_fetch_add(word(slot, kEmpty), 1u, __ATOMIC_RELAXED);
@@ -84,22 +84,35 @@ struct HandoffRing {
 };
 
 // One lane's share of the consumer work on one tile: one row.
+//
+// The row is read in 16-byte chunks.  Each chunk is fetched with an LDS-DMA
+// load into the lane's 16 bytes of one of its wave's landing slots, then
+// waited for, read back, and folded in.  Going through LDS (like the K-loop
+// ring) keeps every wait explicit: the compiler never sees an outstanding
+// load, so it never answers one with a vmcnt(0) that would also drain the
+// ring.  Inside the K loop one chunk is fetched per iteration, before the
+// iteration's stage loads, and folded in one iteration later, after the next
+// iteration's stage loads; after the loop the rest of the row is drained
+// with kConsumerDepth fetches in flight.
 struct TileConsumer {
-  static constexpr int kChunks = kTileN / 8;  // 16-byte chunks per tile row
-  const unsigned short* src;   // D row, first column of the tile (NULL: no row)
-  unsigned short* dst;         // D_copy row, same place
-  float* sum_out;
-  float* max_out;
+  __amdgpu_buffer_rsrc_t rsrc;  // D from the tile's first row and column
+  uint32_t row_off;            // byte offset of this lane's row in rsrc (kOobOffset: no row)
+  unsigned short* dst;         // D_copy row, first column of the tile
+  int64_t stat;                // index of this row's entry in row_sum / row_max
   int ncols;                   // valid columns of the tile
-  int step;                    // next step, 0 .. chunks()
+  int fetched;                 // chunks fetched so far
+  int done;                    // chunks folded in so far
   int slot;
   bool active;
+  bool has_row;
   float sum, mx;
-  u32x4 data;                  // chunk fetched by the previous step
 
   __device__ __forceinline__ int chunks() const { return (ncols + 7) >> 3; }
-
   __device__ __forceinline__ void idle() { active = false; }
+
+  __device__ __forceinline__ static uint32_t landing(int wave, int c) {
+    return kConsumerSlotOffset + (wave * kConsumerDepth + (c % kConsumerDepth)) * kConsumerSlotBytes;
+  }
 
   // Wait for the use-th commit of `slot`, then set up this lane's row.
   __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int wave,
@@ -107,50 +120,29 @@ struct TileConsumer {
     slot = slot_;
     const int tile_id = HandoffRing::wait(slot, use);
     const TileCoord t = tile_of(tile_id, a);
-    const int64_t row = (int64_t)t.tm * kTileM + wave * 64 + lane;
-    const int64_t col0 = (int64_t)t.tn * kTileN;
-    const int64_t left = a.N - col0;
+    const int64_t r0 = (int64_t)t.tm * kTileM;
+    const int64_t c0 = (int64_t)t.tn * kTileN;
+    const int r = wave * 64 + lane;
+    const int64_t left = a.N - c0;
     ncols = (int)(left < kTileN ? left : kTileN);
-    if (row < a.M) {
-      src = static_cast<const unsigned short*>(a.D) + row * a.ldd + col0;
-      dst = static_cast<unsigned short*>(a.D_copy) + row * a.ldd + col0;
-      sum_out = a.row_sum + row * a.stat_ld + t.tn;
-      max_out = a.row_max + row * a.stat_ld + t.tn;
-    } else {
-      src = nullptr;
-    }
-    step = 0;
+    const unsigned short* base = static_cast<const unsigned short*>(a.D) + r0 * a.ldd + c0;
+    int64_t bytes = ((a.M - 1 - r0) * a.ldd + (a.N - c0)) * 2;
+    bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see OperandLoader::issue
+    rsrc = make_rsrc(base, (uint32_t)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes));
+    has_row = r0 + r < a.M;
+    row_off = has_row ? (uint32_t)(r * a.ldd * 2) : kOobOffset;
+    dst = static_cast<unsigned short*>(a.D_copy) + (r0 + r) * a.ldd + c0;
+    stat = (r0 + r) * a.stat_ld + t.tn;
+    fetched = 0;
+    done = 0;
     sum = 0.0f;
     mx = -__builtin_inff();
     active = true;
   }
 
-  // Fetch chunk c of the row.  A whole chunk is one 16-byte load issued as
-  // inline assembly, so that the compiler does not answer its result with a
-  // vmcnt(0) that would also drain the K loop's LDS-DMA loads; advance()
-  // waits for it explicitly.  The partial last chunk of a ragged tile uses
-  // element loads the compiler tracks itself.
-  __device__ __forceinline__ u32x4 fetch(int c) const {
-    const int col = 8 * c;
-    u32x4 v;
-    if (col + 8 <= ncols) {
-      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(src + col) : "memory");
-      return v;
-    }
-    v = u32x4{0, 0, 0, 0};
-    for (int e = 0; col + e < ncols; ++e) v[e >> 1] |= (uint32_t)src[col + e] << (16 * (e & 1));
-    return v;
-  }
-
-  // Wait until the chunk fetched by the previous step has arrived.  The
-  // vector memory operations issued since then are the stage loads of this
-  // K iteration (8, or none), and they complete after it (in order).
-  __device__ __forceinline__ void wait_fetched(bool stage_loads_since) {
-    if (stage_loads_since) {
-      asm volatile("s_waitcnt vmcnt(8)" : "+v"(data) : : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(data) : : "memory");
-    }
+  __device__ __forceinline__ void fetch(int wave) {
+    const int c = fetched++;
+    dma16(rsrc, lds_at(landing(wave, c)), row_off == kOobOffset ? kOobOffset : row_off + 16 * c);
   }
 
   __device__ __forceinline__ void absorb(int c, u32x4 v) {
@@ -175,31 +167,58 @@ struct TileConsumer {
     }
   }
 
-  // One step: fold in the chunk fetched last time and fetch the next one.
-  // stage_loads_since: the K loop issued stage loads since the last step.
-  __device__ __forceinline__ void advance(int lane, bool stage_loads_since) {
-    if (!active) return;
-    const int nc = chunks();
-    if (src) {
-      if (step > 0) {
-        wait_fetched(stage_loads_since);
-        absorb(step - 1, data);
-      }
-      if (step < nc) data = fetch(step);
-    }
-    ++step;
-    if (step > nc) {
-      if (src) {
-        *sum_out = sum;
-        *max_out = mx;
+  // Fold in the oldest fetched chunk (its fetch must have completed).
+  __device__ __forceinline__ void fold(const KernelArgs& a, int wave, int lane) {
+    compiler_fence();
+    const int c = done++;
+    const u32x4 v = *(const MIGEMM_LDS u32x4*)lds_at(landing(wave, c) + 16 * lane);
+    if (has_row) absorb(c, v);
+    wait_lgkmcnt<0>();  // the read is done before the landing slot is refilled
+    if (done == chunks()) {
+      if (has_row) {
+        a.row_sum[stat] = sum;
+        a.row_max[stat] = mx;
       }
       active = false;
       HandoffRing::release(slot, lane);
     }
   }
 
-  __device__ __forceinline__ void drain(int lane) {
-    while (active) advance(lane, false);
+  // K-loop hook, once per iteration: fold in the chunk fetched one iteration
+  // earlier, then fetch the next.  Since that fetch the wave has issued only
+  // the 8 loads of one K stage (eight_since) or none, plus at most a store,
+  // all younger than it; vector memory operations complete in order, so
+  // vmcnt(8) covers the fetch without forcing those stage loads to land.
+  __device__ __forceinline__ void step(const KernelArgs& a, int wave, int lane, bool eight_since) {
+    if (!active) return;
+    if (fetched > done) {
+      if (eight_since) {
+        wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      fold(a, wave, lane);
+    }
+    if (active && fetched < chunks()) fetch(wave);
+  }
+
+  // After the K loop: finish the row with up to kConsumerDepth fetches in
+  // flight.  newer = fetches issued after the one being waited for.
+  __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
+    while (active) {
+      while (fetched < chunks() && fetched - done < kConsumerDepth) fetch(wave);
+      const int newer = fetched - done - 1;
+      if (newer >= 3) {
+        wait_vmcnt<3>();
+      } else if (newer == 2) {
+        wait_vmcnt<2>();
+      } else if (newer == 1) {
+        wait_vmcnt<1>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      fold(a, wave, lane);
+    }
   }
 };
 

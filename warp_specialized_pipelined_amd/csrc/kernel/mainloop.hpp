@@ -25,11 +25,14 @@
 //   K-contiguous operand: 256 rows x 64 bytes of K, the four 16-byte chunks
 //     of row r stored in the order c ^ swz_k(r), so that the eight rows read
 //     by one group of lanes fall on distinct banks.
-//   MN-contiguous operand: (64 / elem_size) rows of K, each 256 elements of
-//     M or N wide.
-// The swizzle is applied on the global side: LDS-DMA writes lane i's 16
-// bytes to a fixed LDS slot, so each lane fetches the chunk that belongs in
-// its slot.
+//   MN-contiguous operand: 8 panels of 32 columns (of M or N), each panel
+//     holding the stage's (64 / elem_size) K rows back to back, 32 elements
+//     per row (2 KiB per panel).  The transposing reads of one half-wave
+//     then cover 256 consecutive bytes -- every bank once -- and every
+//     fragment of a wave sits at a constant offset from its first one.
+// The K-contiguous swizzle is applied on the global side: LDS-DMA writes
+// lane i's 16 bytes to a fixed LDS slot, so each lane fetches the chunk that
+// belongs in its slot.
 #pragma once
 
 #include <type_traits>
@@ -50,14 +53,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ int swz_k(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// MN-contiguous stages are read with the transposing LDS loads, which fetch
-// 8-byte pieces of 4 (bf16) or 8 (e4m3) consecutive K rows at once; XOR-ing
-// the 16-byte chunk index with a function of the K row puts those rows on
-// different banks.
-template <int ES>
-__device__ __forceinline__ int swz_mn(int krow) {
-  return ES == 2 ? (krow & 7) << 2 : (krow & 7) << 1;
-}
+// Bytes of one MN-contiguous panel: 32 columns by a stage's K rows.
+constexpr int kPanelBytes = 32 * kStageKBytes;  // 2 KiB
 
 // One operand's share of the ring: where this wave's 4 loads per stage come
 // from and go to.  ES = element size in bytes, KMAJ = K is the contiguous
@@ -89,24 +86,40 @@ struct OperandLoader {
         kpos[j] = c * kElemsPerChunk;
       }
     } else {
-      constexpr int kRowBytes = kTileM * ES;           // 512 (bf16) or 256 (e4m3)
-      constexpr int kChunksPerRow = kRowBytes / 16;    // 32 or 16
-      constexpr int kRowsPerLoad = 1024 / kRowBytes;   // 2 or 4
+      // Load idx = 4 * wave + j fills half (idx & 1) of panel (idx >> 1):
+      // kRowsPerLoad K rows of the panel's 32 columns, each row read by
+      // kLanesPerRow lanes.
+      constexpr int kLanesPerRow = 32 * ES / 16;         // 4 (bf16) or 2 (e4m3)
+      constexpr int kRowsPerLoad = 64 / kLanesPerRow;    // 16 or 32
       tile_base = p + origin * ES;
       kstep_bytes = (int64_t)kBK * ld * ES;
       bytes_left = bytes - origin * ES;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int krow = (wave * 4 + j) * kRowsPerLoad + lane / kChunksPerRow;
-        const int c = (lane % kChunksPerRow) ^ swz_mn<ES>(krow);
-        off[j] = (uint32_t)(krow * ld * ES) + (uint32_t)(c * 16);
+        const int idx = wave * 4 + j;
+        const int krow = (idx & 1) * kRowsPerLoad + lane / kLanesPerRow;
+        const int col = (idx >> 1) * 32 + (lane % kLanesPerRow) * kElemsPerChunk;
+        off[j] = (uint32_t)(krow * ld * ES) + (uint32_t)(col * ES);
         kpos[j] = krow;
       }
     }
   }
 
+  // Issue load j (0..3) of this wave's 4 loads of K stage `kt` into ring
+  // slot `slot`.  `half` is 0 for A and kOperandStageBytes for B.
+  __device__ __forceinline__ void issue_one(int kt, int slot, int half, int64_t K, int wave,
+                                            int j) const {
+    const int64_t step = (int64_t)kt * kstep_bytes;
+    int64_t left = (bytes_left - step + 15) & ~(int64_t)15;
+    left = left < 0 ? 0 : (left > 0x7FFFFFF0 ? 0x7FFFFFF0 : left);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_base + step, (uint32_t)left);
+    const int64_t krem64 = K - (int64_t)kt * kBK;
+    const int krem = krem64 > kBK ? kBK : (int)krem64;
+    const uint32_t v = (kpos[j] < krem) ? off[j] : kOobOffset;
+    dma16(r, lds_at(slot * kStageBytes + half + (wave * 4 + j) * 1024), v);
+  }
+
   // Issue this wave's 4 loads of K stage `kt` into ring slot `slot`.
-  // `half` is 0 for A and kOperandStageBytes for B.
   __device__ __forceinline__ void issue(int kt, int slot, int half, int64_t K, int wave) const {
     const int64_t step = (int64_t)kt * kstep_bytes;
     // Buffer range checks work per dword, so an operand whose last row ends
@@ -129,37 +142,54 @@ struct OperandLoader {
 
 // Fragment reads.  A "fragment" is what one lane feeds one 32 x 32 MFMA: 32
 // bytes of K (fp8) or 16 bytes (bf16, one of two k-steps per stage) of one
-// row of A or one column of B.
+// row of A or one column of B.  Each reader keeps the lane's byte offsets of
+// its wave's first 32-row (or -column) block; block BLK and k-step KS sit at
+// a compile-time distance from them, which the LDS instructions take as an
+// immediate offset, so a stage costs one address add per offset.
 template <int ES, bool KMAJ>
 struct FragReader;
 
-// K-contiguous bf16: one ds_read_b128 per fragment.
+// K-contiguous bf16: one ds_read_b128 per fragment.  Rows of a 32-row block
+// start 32 rows apart, so the swizzle depends on the lane alone.
 template <>
 struct FragReader<2, true> {
   typedef bf16x8 frag_t;
   static constexpr int kSteps = 2;  // 32 k per stage, 16 per MFMA
   static constexpr int kReads = 1;  // LDS instructions per fragment
-  __device__ __forceinline__ static frag_t read(uint32_t opnd_base, int row0, int ks, int lane) {
-    const int r = row0 + (lane & 31);
-    const int c = 2 * ks + (lane >> 5);
-    const lds_u8* p = lds_at(opnd_base + r * kStageKBytes + ((c ^ swz_k(r)) << 4));
-    return *reinterpret_cast<const MIGEMM_LDS frag_t*>(p);
+  uint32_t off[2];                  // per k-step
+  __device__ __forceinline__ void init(int row0, int lane) {
+    const int l = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      off[ks] = (row0 + l) * kStageKBytes + (((2 * ks + (lane >> 5)) ^ swz_k(l)) << 4);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
+    return *reinterpret_cast<const MIGEMM_LDS frag_t*>(
+        lds_at(opnd_base + off[KS] + BLK * 32 * kStageKBytes));
   }
 };
 
-// K-contiguous e4m3: two ds_read_b128 per fragment.
+// K-contiguous e4m3: two ds_read_b128 per fragment (the two 16-byte halves
+// of the lane's 32 bytes of K).
 template <>
 struct FragReader<1, true> {
   typedef i32x8 frag_t;
   static constexpr int kSteps = 1;  // 64 k per stage, 64 per MFMA
   static constexpr int kReads = 2;
-  __device__ __forceinline__ static frag_t read(uint32_t opnd_base, int row0, int ks, int lane) {
-    (void)ks;
-    const int r = row0 + (lane & 31);
-    const int c0 = 2 * (lane >> 5);
-    const lds_u8* rowp = lds_at(opnd_base + r * kStageKBytes);
-    const i32x4 lo = *reinterpret_cast<const MIGEMM_LDS i32x4*>(rowp + (((c0) ^ swz_k(r)) << 4));
-    const i32x4 hi = *reinterpret_cast<const MIGEMM_LDS i32x4*>(rowp + (((c0 + 1) ^ swz_k(r)) << 4));
+  uint32_t off[2];                  // per half
+  __device__ __forceinline__ void init(int row0, int lane) {
+    const int l = lane & 31;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      off[h] = (row0 + l) * kStageKBytes + (((2 * (lane >> 5) + h) ^ swz_k(l)) << 4);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
+    const i32x4 lo = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
+        lds_at(opnd_base + off[0] + BLK * 32 * kStageKBytes));
+    const i32x4 hi = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
+        lds_at(opnd_base + off[1] + BLK * 32 * kStageKBytes));
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 };
@@ -168,25 +198,30 @@ struct FragReader<1, true> {
 // group of 16 lanes the instruction reads a 4 x 16 block of bf16 (lanes
 // 4r..4r+3 each fetch 4 consecutive elements of row r) and hands lane i
 // column i of the block.  Rows are K and columns are M or N here, so each
-// lane receives 4 consecutive k of its own column.
+// lane receives 4 consecutive k of its own column: lane l gets column l % 32
+// of the block and k = 8 (l / 32) + 0..3 (first read) and + 4..7 (second).
 template <>
 struct FragReader<2, false> {
   typedef bf16x8 frag_t;
   static constexpr int kSteps = 2;
   static constexpr int kReads = 2;
-  __device__ __forceinline__ static const lds_u8* at(uint32_t base, int k, int n) {
-    return lds_at(base + k * (kTileM * 2) + (((n >> 3) ^ swz_mn<2>(k)) << 4) + ((n & 7) << 1));
-  }
-  __device__ __forceinline__ static frag_t read(uint32_t opnd_base, int col0, int ks, int lane) {
+  static constexpr int kRowBytes = 64;  // one K row of a panel
+  uint32_t off;
+  __device__ __forceinline__ void init(int col0, int lane) {
     const int g = lane >> 4, t = lane & 15;
-    const int n = col0 + 16 * (g & 1) + 4 * (t & 3);
-    const int k = 16 * ks + 8 * (g >> 1) + (t >> 2);
+    const int n = 16 * (g & 1) + 4 * (t & 3);  // column within the panel
+    const int k = 8 * (g >> 1) + (t >> 2);
+    off = (col0 / 32) * kPanelBytes + k * kRowBytes + n * 2;
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)(at(opnd_base, k, n)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)(at(opnd_base, k + 4, n)));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
+    constexpr uint32_t c = BLK * kPanelBytes + 16 * KS * kRowBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off + c));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off + c + 4 * kRowBytes));
     const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(frag_t, v);
   }
@@ -195,27 +230,31 @@ struct FragReader<2, false> {
 // MN-contiguous e4m3: four ds_read_b64_tr_b8 per fragment.  Within each
 // group of 16 lanes the instruction reads an 8 x 16 block of bytes (lanes 2r
 // and 2r+1 fetch the two halves of row r) and hands lane i column i, i.e. 8
-// consecutive k of its own column.
+// consecutive k of its own column: lane l gets column l % 32 of the block and
+// k = 32 (l / 32) + 8 h + 0..7 from read h.
 template <>
 struct FragReader<1, false> {
   typedef i32x8 frag_t;
   static constexpr int kSteps = 1;
   static constexpr int kReads = 4;
-  __device__ __forceinline__ static const lds_u8* at(uint32_t base, int k, int n) {
-    return lds_at(base + k * kTileM + (((n >> 4) ^ swz_mn<1>(k)) << 4) + (n & 15));
-  }
-  __device__ __forceinline__ static frag_t read(uint32_t opnd_base, int col0, int ks, int lane) {
-    (void)ks;
+  static constexpr int kRowBytes = 32;
+  uint32_t off;
+  __device__ __forceinline__ void init(int col0, int lane) {
     const int g = lane >> 4, t = lane & 15;
-    const int n = col0 + 16 * (g & 1) + 8 * (t & 1);
+    const int n = 16 * (g & 1) + 8 * (t & 1);
     const int k = 32 * (g >> 1) + (t >> 1);
+    off = (col0 / 32) * kPanelBytes + k * kRowBytes + n;
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
     i32x8 v;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MIGEMM_LDS i32x2*)(at(opnd_base, k + 8 * h, n)));
+    static_for<0, 4>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (MIGEMM_LDS i32x2*)lds_at(opnd_base + off + BLK * kPanelBytes + 8 * h * kRowBytes));
       v[2 * h] = w[0];
       v[2 * h + 1] = w[1];
-    }
+    });
     return v;
   }
 };
@@ -257,6 +296,8 @@ struct FragHalves {
   static constexpr int kPerHalf = kBf16 ? 4 : 2;   // A (and B) fragments per half
   typename RA::frag_t a[2][kPerHalf];
   typename RB::frag_t b[2][kPerHalf];
+  RA ra;
+  RB rb;
 
   // LDS read instructions of one half, and MFMAs of each phase.
   static constexpr int kReadInsts = kPerHalf * (RA::kReads + RB::kReads);
@@ -264,17 +305,25 @@ struct FragHalves {
   static constexpr int kPhase1 = kBf16 ? 0 : 8;
   static constexpr int kPhase2 = kBf16 ? 16 : 4;
 
-  __device__ __forceinline__ void read(int h, int slot, int wm, int wn, int lane) {
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    ra.init(wm * kWaveTile, lane);
+    rb.init(wn * kWaveTile, lane);
+  }
+
+  // Fragments [Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ) of half H from
+  // ring slot `slot`.
+  template <int H, int Q, int NQ>
+  __device__ __forceinline__ void read_part(int slot) {
     const uint32_t a_base = slot * kStageBytes;
     const uint32_t b_base = a_base + kOperandStageBytes;
-#pragma unroll
-    for (int x = 0; x < kPerHalf; ++x) {
-      // bf16: block x of k-step h; e4m3: block 2h + x of the single k-step
-      const int blk = kBf16 ? x : 2 * h + x;
-      const int ks = kBf16 ? h : 0;
-      a[h][x] = RA::read(a_base, wm * kWaveTile + 32 * blk, ks, lane);
-      b[h][x] = RB::read(b_base, wn * kWaveTile + 32 * blk, ks, lane);
-    }
+    static_for<Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ>([&](auto xc) {
+      constexpr int x = decltype(xc)::value;
+      // bf16: block x of k-step H; e4m3: block 2H + x of the single k-step
+      constexpr int blk = kBf16 ? x : 2 * H + x;
+      constexpr int ks = kBf16 ? H : 0;
+      a[H][x] = ra.template read<blk, ks>(a_base);
+      b[H][x] = rb.template read<blk, ks>(b_base);
+    });
   }
 
   // MFMAs [FIRST, FIRST + COUNT) of phase P (all indices compile-time, so
@@ -325,26 +374,30 @@ __device__ __forceinline__ void wait_stages_in_flight(int pending) {
 // phases of the K loop stay in the order written.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Work that rides along in the K loop: called once per stage, after the
-// stage's loads are issued (the flag says whether any were).
+// Work that rides along in the K loop: step() is called once per iteration,
+// right after the barrier.
 struct NoSideWork {
-  __device__ __forceinline__ void advance(int, bool) {}
+  __device__ __forceinline__ void step(const KernelArgs&, int, int, bool) {}
 };
 
 // The whole K loop of one output tile.
 //
 // Iteration kt works on stage kt, whose half-0 fragments were read during the
 // previous iteration.  The workgroup barrier certifies stage kt+1 (one ahead):
-//   phase 0: MFMAs on half 0, under which half 1 of stage kt is read;
-//   phase 1: MFMAs needing both halves (e4m3 only);
+//   phase 0: MFMAs on half 0, under which half 1 of stage kt is read; the B
+//            loads of stage kt+2 go out one per 4 MFMAs (bf16);
+//   phase 1: MFMAs needing both halves (e4m3 only), with those B loads;
 //   sync:    wait for this wave's loads of stage kt+1, barrier -- now stage
 //            kt+1 is in LDS for every wave, and every wave is done reading
 //            stage kt-1;
-//   phase 2: MFMAs on half 1; the loads of stage kt+3 (into stage kt-1's
-//            slot) are issued between the first of them, and half 0 of stage
-//            kt+1 is read under the rest.
-// So the MFMA pipe does not wait on the barrier or on a first LDS read, only
-// 64 VGPRs hold fragments, and each stage's loads get two iterations to land.
+//   phase 2: the side work steps once; MFMAs on half 1, with the A loads of
+//            stage kt+3 one per 4 MFMAs (e4m3: one per MFMA) and half 0 of
+//            stage kt+1 read under them.
+// Each stage's loads are thus spread over two iterations instead of leaving
+// in one burst after the barrier, when all four waves would queue 32 of them
+// on the CU's address unit at once and starve the MFMA pipe.  Stage s's A
+// half leaves in iteration s-3 (after barrier s-3 freed stage s-4's slot) and
+// its B half in iteration s-2; both are certified in iteration s-1.
 template <int ES, bool AK, bool BK, class SideWork>
 __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn, int wave,
                                          int lane, SideWork& side) {
@@ -357,6 +410,7 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   lb.init(a.B, a.b_bytes, a.ldb, (int64_t)tn * kTileN, wave, lane);
   const int wm = wave >> 1, wn = wave & 1;
   const int KT = (int)((a.K + kBK - 1) / kBK);
+  constexpr int kB = kOperandStageBytes;
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -364,45 +418,78 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     for (int j = 0; j < 4; ++j) acc.v[i][j] = f32x16{};
 
   FH f;
+  f.init(wm, wn, lane);
   if (KT > 0) {
     // Prologue: stages 0..2 in flight, stage 0 certified, its half 0 read.
     for (int s = 0; s < kStages - 1 && s < KT; ++s) {
       la.issue(s, s, 0, a.K, wave);
-      lb.issue(s, s, kOperandStageBytes, a.K, wave);
+      lb.issue(s, s, kB, a.K, wave);
     }
     wait_stages_in_flight(min(kStages - 2, KT - 1));
     barrier();
-    f.read(0, 0, wm, wn, lane);
+    f.template read_part<0, 0, 1>(0);
   }
   for (int kt = 0; kt < KT; ++kt) {
     // Every iteration has the same shape (no branch around MFMAs, so the
-    // accumulators never meet at a join): in the last one the barrier is
+    // accumulators never meet at a join): in the last ones the barrier is
     // redundant and the half-0 read fetches bytes nobody uses.
     const int slot = kt % kStages;
-    sched_fence();
-    f.read(1, slot, wm, wn, lane);
-    f.template mma<0, 0, FH::kPhase0>(acc);
-    interleave_mfma_reads<FH::kPhase0, FH::kReadInsts>();
-    sched_fence();
-    if constexpr (FH::kPhase1 > 0) {
-      f.template mma<1, 0, FH::kPhase1>(acc);
+    const int sb = kt + 2;                       // stage whose B half leaves now
+    const bool b_due = kt >= 1 && sb < KT;       // (stage 2's left in the prologue)
+    const int sa = kt + 3;                       // stage whose A half leaves now
+    const bool a_due = sa < KT;
+    const int nslot = (kt + 1) % kStages;
+    if constexpr (FH::kBf16) {
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        if (b_due) lb.issue_one(sb, sb % kStages, kB, a.K, wave, q);
+        f.template read_part<1, q, 4>(slot);
+        f.template mma<0, 4 * q, 4>(acc);
+        interleave_mfma_reads<4, FH::kReadInsts / 4>();
+      });
+    } else {
       sched_fence();
+      f.template read_part<1, 0, 1>(slot);
+      f.template mma<0, 0, FH::kPhase0>(acc);
+      interleave_mfma_reads<FH::kPhase0, FH::kReadInsts>();
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        if (b_due) lb.issue_one(sb, sb % kStages, kB, a.K, wave, q);
+        f.template mma<1, 2 * q, 2>(acc);
+      });
     }
-    // Stage kt+2 may stay in flight.  Any other vector memory operation
-    // issued after stage kt+1's loads only makes this wait stricter: vector
-    // memory operations complete in order.
-    wait_stages_in_flight(KT - 2 - kt);
-    barrier();
-    const int s3 = kt + kStages - 1;
-    f.template mma<2, 0, 1>(acc);
-    if (s3 < KT) la.issue(s3, s3 % kStages, 0, a.K, wave);
-    f.template mma<2, 1, 1>(acc);
-    if (s3 < KT) lb.issue(s3, s3 % kStages, kOperandStageBytes, a.K, wave);
-    side.advance(lane, s3 < KT);
     sched_fence();
-    f.read(0, (kt + 1) % kStages, wm, wn, lane);
-    f.template mma<2, 2, FH::kPhase2 - 2>(acc);
-    interleave_mfma_reads<FH::kPhase2 - 2, FH::kReadInsts>();
+    // Stage kt+1's last loads (its B half) left in iteration kt-1, or in the
+    // prologue; younger than them are at most the 8 loads of stage kt+2, which
+    // may stay in flight.  Any other vector memory operation issued after
+    // them only makes this wait stricter: vector memory operations complete
+    // in order.
+    wait_stages_in_flight(min(KT - 2 - kt, 1));
+    barrier();
+    // Since the side work's previous step, this wave has issued exactly the
+    // 8 stage loads of stage kt+2 (if that stage exists).
+    side.step(a, wave, lane, kt + 2 < KT);
+    if constexpr (FH::kBf16) {
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        if (a_due) la.issue_one(sa, sa % kStages, 0, a.K, wave, q);
+        f.template read_part<0, q, 4>(nslot);
+        f.template mma<2, 4 * q, 4>(acc);
+        interleave_mfma_reads<4, FH::kReadInsts / 4>();
+      });
+    } else {
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        if (a_due) la.issue_one(sa, sa % kStages, 0, a.K, wave, q);
+        f.template read_part<0, q, 4>(nslot);
+        f.template mma<2, q, 1>(acc);
+        interleave_mfma_reads<1, FH::kReadInsts / 2>();
+      });
+    }
   }
   // Every wave is done with the ring before anyone reuses it.
   sched_fence();

@@ -26,11 +26,21 @@ constexpr int kRingBytes = kStages * kStageBytes;          // 128 KiB
 constexpr int kStagingRowBytes = kWaveTile * 2 + 16;                 // 272
 constexpr int kStagingWaveBytes = kWaveTile * kStagingRowBytes;      // 34816
 constexpr int kStagingBytes = kWaves * kStagingWaveBytes;            // 139264
+// Consumer-stage landing slots: per wave kConsumerDepth slots of 1 KiB (16
+// bytes per lane), past both the ring and the staging area.  The consumer
+// fetches while the K loop runs (so the slots must not overlap the ring),
+// and one wave may still be draining its consumer work while another
+// already stages its epilogue (so they must not overlap the staging either).
+constexpr int kConsumerDepth = 4;
+constexpr int kConsumerSlotOffset = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
+constexpr int kConsumerSlotBytes = 64 * 16;
+constexpr int kConsumerEnd = kConsumerSlotOffset + kWaves * kConsumerDepth * kConsumerSlotBytes;
 // Tile hand-off ring: two slots of {tile id, full count, empty count}.
 constexpr int kHandoffSlots = 2;
-constexpr int kHandoffOffset = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
+constexpr int kHandoffOffset = kConsumerEnd;
 constexpr int kHandoffBytes = 64;
 constexpr int kLdsBytes = kHandoffOffset + kHandoffBytes;
+static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 
 struct KernelArgs {
   const void* A;       // operand storage (after any swap of A and B)
