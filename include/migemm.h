@@ -104,7 +104,7 @@ typedef struct migemm_plan_info {
   int64_t tiles_m, tiles_n, num_tiles;
   int32_t grid;            /* persistent workgroups launched */
   int32_t block_threads;   /* threads per workgroup (4 waves of 64) */
-  int32_t lds_bytes;       /* LDS per workgroup */
+  int32_t lds_bytes;       /* LDS per workgroup (of the kernel gemm_run launches) */
   int32_t stages;          /* depth of the main-loop LDS ring */
   int32_t tile_m, tile_n, tile_k;
   int32_t swapped;         /* 1: column-major D, computed as D^T = B^T A^T */

@@ -144,7 +144,7 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, desc->device) != hipSuccess) return MIGEMM_ERR_DEVICE;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MIGEMM_ERR_DEVICE;
-  if (prop.sharedMemPerBlock < (size_t)migemm::kLdsBytes) return MIGEMM_ERR_DEVICE;
+  if (prop.sharedMemPerBlock < (size_t)migemm::kLdsLimit) return MIGEMM_ERR_DEVICE;
 
   migemm_plan* p = new (std::nothrow) migemm_plan;
   if (!p) return MIGEMM_ERR_INVALID_ARG;
@@ -203,8 +203,8 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
                  "grid=%d group_m=%d lds=%d stages=%d cus=%d\n",
                  (long long)c.M, (long long)c.N, (long long)c.K, es,
                  p->sel.a_kmajor ? "K-contig" : "M-contig", p->sel.b_kmajor ? "K-contig" : "N-contig",
-                 (int)c.swapped, a.tiles_m, a.tiles_n, grid, a.group_m, migemm::kLdsBytes,
-                 migemm::kStages, p->cu_count);
+                 (int)c.swapped, a.tiles_m, a.tiles_n, grid, a.group_m,
+                 migemm::kernel_lds_bytes(p->sel), migemm::kStages, p->cu_count);
   }
   *out = p;
   return MIGEMM_OK;
@@ -223,7 +223,7 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
   out->num_tiles = p->base.num_tiles;
   out->grid = p->grid;
   out->block_threads = migemm::kThreads;
-  out->lds_bytes = migemm::kLdsBytes;
+  out->lds_bytes = migemm::kernel_lds_bytes(p->sel);
   out->stages = migemm::kStages;
   out->tile_m = migemm::kTileM;
   out->tile_n = migemm::kTileN;

@@ -92,13 +92,18 @@ static kernel_fn select(const KernelSelect& s) {
                            : pick<1>(s.a_kmajor, s.b_kmajor, s.consumer);
 }
 
+int kernel_lds_bytes(const KernelSelect& sel) {
+  return sel.consumer ? kConsumerLdsBytes : kPlainLdsBytes;
+}
+
+
 hipError_t prepare_kernel(const KernelSelect& sel) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(select(sel)),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kernel_lds_bytes(sel));
 }
 
 hipError_t launch_gemm(const KernelSelect& sel, const KernelArgs& args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(select(sel), dim3(grid), dim3(kThreads), kLdsBytes, stream, args);
+  hipLaunchKernelGGL(select(sel), dim3(grid), dim3(kThreads), kernel_lds_bytes(sel), stream, args);
   return hipGetLastError();
 }
 

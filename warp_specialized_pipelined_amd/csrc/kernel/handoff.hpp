@@ -35,6 +35,7 @@
 
 #include "gfx950.hpp"
 #include "params.hpp"
+#include "mainloop.hpp"
 #include "scheduler.hpp"
 
 namespace migemm {
@@ -90,10 +91,10 @@ struct HandoffRing {
 // waited for, read back, and folded in.  Going through LDS (like the K-loop
 // ring) keeps every wait explicit: the compiler never sees an outstanding
 // load, so it never answers one with a vmcnt(0) that would also drain the
-// ring.  Inside the K loop one chunk is fetched per iteration, before the
-// iteration's stage loads, and folded in one iteration later, after the next
-// iteration's stage loads; after the loop the rest of the row is drained
-// with kConsumerDepth fetches in flight.
+// ring.  Inside the K loop one chunk is fetched per iteration, just before
+// the iteration's stage loads, and folded in one iteration later, when only
+// those 8 stage loads are younger than it; after the loop the rest of the
+// row is drained with kConsumerDepth fetches in flight.
 struct TileConsumer {
   __amdgpu_buffer_rsrc_t rsrc;  // D from the tile's first row and column
   uint32_t row_off;            // byte offset of this lane's row in rsrc (kOobOffset: no row)
@@ -185,14 +186,14 @@ struct TileConsumer {
   }
 
   // K-loop hook, once per iteration: fold in the chunk fetched one iteration
-  // earlier, then fetch the next.  Since that fetch the wave has issued only
-  // the 8 loads of one K stage (eight_since) or none, plus at most a store,
-  // all younger than it; vector memory operations complete in order, so
-  // vmcnt(8) covers the fetch without forcing those stage loads to land.
-  __device__ __forceinline__ void step(const KernelArgs& a, int wave, int lane, bool eight_since) {
+  // earlier, then fetch the next.  Since that fetch the wave has issued the
+  // `since` (8) stage loads of one iteration, all younger than it; vector
+  // memory operations complete in order, so vmcnt(8) covers the fetch
+  // without forcing those stage loads to land.
+  __device__ __forceinline__ void step(const KernelArgs& a, int wave, int lane, int since) {
     if (!active) return;
     if (fetched > done) {
-      if (eight_since) {
+      if (since >= 8) {
         wait_vmcnt<8>();
       } else {
         wait_vmcnt<0>();
@@ -208,6 +209,7 @@ struct TileConsumer {
     while (active) {
       while (fetched < chunks() && fetched - done < kConsumerDepth) fetch(wave);
       const int newer = fetched - done - 1;
+      static_assert(kConsumerDepth <= 4, "drain waits are written for up to 4 fetches in flight");
       if (newer >= 3) {
         wait_vmcnt<3>();
       } else if (newer == 2) {

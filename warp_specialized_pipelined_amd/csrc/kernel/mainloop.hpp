@@ -23,16 +23,23 @@
 //
 // LDS layout of one stage (32 KiB):  [A: 16 KiB][B: 16 KiB].
 //   K-contiguous operand: 256 rows x 64 bytes of K, the four 16-byte chunks
-//     of row r stored in the order c ^ swz_k(r), so that the eight rows read
-//     by one group of lanes fall on distinct banks.
-//   MN-contiguous operand: 8 panels of 32 columns (of M or N), each panel
-//     holding the stage's (64 / elem_size) K rows back to back, 32 elements
-//     per row (2 KiB per panel).  The transposing reads of one half-wave
-//     then cover 256 consecutive bytes -- every bank once -- and every
-//     fragment of a wave sits at a constant offset from its first one.
-// The K-contiguous swizzle is applied on the global side: LDS-DMA writes
+//     of row r stored in the order c ^ swz_k(r).
+//   MN-contiguous operand: panels of 128 bytes of M or N (64 bf16 or 128
+//     e4m3 columns), each panel holding the stage's (64 / elem_size) K rows
+//     back to back, with the 16-byte chunks of row k permuted by swz_mn(k).
+// Both swizzles make the fragment reads of one instruction hit every LDS
+// bank equally often (measured on gfx950: a K-major 16-byte read then takes
+// ~4.5 cycles per instruction instead of 8, and a transposing read ~3.8
+// instead of 4.5-8).  They are applied on the global side: LDS-DMA writes
 // lane i's 16 bytes to a fixed LDS slot, so each lane fetches the chunk that
 // belongs in its slot.
+//
+// Global side: every LDS-DMA instruction reads whole 128-byte segments (8
+// lanes) for MN-contiguous operands.  The memory pipeline serves requests,
+// not bytes: loads made of 64-byte segments reach only about half the L2 and
+// HBM throughput of 128-byte ones (measured: ~18 vs ~36 TB/s from L2 over
+// the chip).  K-contiguous operands read 64-byte segments (one stage holds
+// 64 bytes of K per row).
 #pragma once
 
 #include <type_traits>
@@ -51,10 +58,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// K-contiguous: chunk c of row r is stored at chunk c ^ swz_k(r).  Rows of
+// a fragment block start 32 rows apart, so the value depends on the lane
+// alone.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
 
-// Bytes of one MN-contiguous panel: 32 columns by a stage's K rows.
-constexpr int kPanelBytes = 32 * kStageKBytes;  // 2 KiB
+// MN-contiguous: a panel row is 128 bytes of M or N; chunk c of K row k is
+// stored at chunk c ^ swz_mn(k).  bf16 swaps the 64-byte halves of every
+// other pair of rows; e4m3 permutes the four 32-byte pieces.
+template <int ES>
+__device__ __forceinline__ int swz_mn(int k) {
+  return ES == 2 ? ((k >> 1) & 1) << 2 : ((k >> 1) & 3) << 1;
+}
+constexpr int kPanelRowBytes = 128;
+template <int ES>
+struct Panel {
+  static constexpr int kCols = kPanelRowBytes / ES;             // 64 or 128
+  static constexpr int kRows = kStageKBytes / ES;               // K rows: 32 or 64
+  static constexpr int kBytes = kRows * kPanelRowBytes;         // 4 or 8 KiB
+  static constexpr int kLoadsPerPanel = kBytes / 1024;          // 4 or 8
+};
 
 // One operand's share of the ring: where this wave's 4 loads per stage come
 // from and go to.  ES = element size in bytes, KMAJ = K is the contiguous
@@ -86,41 +109,28 @@ struct OperandLoader {
         kpos[j] = c * kElemsPerChunk;
       }
     } else {
-      // Load idx = 4 * wave + j fills half (idx & 1) of panel (idx >> 1):
-      // kRowsPerLoad K rows of the panel's 32 columns, each row read by
-      // kLanesPerRow lanes.
-      constexpr int kLanesPerRow = 32 * ES / 16;         // 4 (bf16) or 2 (e4m3)
-      constexpr int kRowsPerLoad = 64 / kLanesPerRow;    // 16 or 32
+      // Load idx = 4 * wave + j fills K rows 8 (idx % L) .. + 7 of panel
+      // idx / L (L loads per panel): 8 lanes per 128-byte row.
+      typedef Panel<ES> P;
       tile_base = p + origin * ES;
       kstep_bytes = (int64_t)kBK * ld * ES;
       bytes_left = bytes - origin * ES;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = wave * 4 + j;
-        const int krow = (idx & 1) * kRowsPerLoad + lane / kLanesPerRow;
-        const int col = (idx >> 1) * 32 + (lane % kLanesPerRow) * kElemsPerChunk;
+        const int krow = (idx % P::kLoadsPerPanel) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_mn<ES>(krow);
+        const int col = (idx / P::kLoadsPerPanel) * P::kCols + chunk * kElemsPerChunk;
         off[j] = (uint32_t)(krow * ld * ES) + (uint32_t)(col * ES);
         kpos[j] = krow;
       }
     }
   }
 
-  // Issue load j (0..3) of this wave's 4 loads of K stage `kt` into ring
-  // slot `slot`.  `half` is 0 for A and kOperandStageBytes for B.
-  __device__ __forceinline__ void issue_one(int kt, int slot, int half, int64_t K, int wave,
-                                            int j) const {
-    const int64_t step = (int64_t)kt * kstep_bytes;
-    int64_t left = (bytes_left - step + 15) & ~(int64_t)15;
-    left = left < 0 ? 0 : (left > 0x7FFFFFF0 ? 0x7FFFFFF0 : left);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_base + step, (uint32_t)left);
-    const int64_t krem64 = K - (int64_t)kt * kBK;
-    const int krem = krem64 > kBK ? kBK : (int)krem64;
-    const uint32_t v = (kpos[j] < krem) ? off[j] : kOobOffset;
-    dma16(r, lds_at(slot * kStageBytes + half + (wave * 4 + j) * 1024), v);
-  }
-
-  // Issue this wave's 4 loads of K stage `kt` into ring slot `slot`.
-  __device__ __forceinline__ void issue(int kt, int slot, int half, int64_t K, int wave) const {
+  // A buffer resource over the operand from K stage `kt` on, and the K
+  // elements left in that stage (clamped: only "less than kBK or not"
+  // matters).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(int kt, int64_t K, int* krem) const {
     const int64_t step = (int64_t)kt * kstep_bytes;
     // Buffer range checks work per dword, so an operand whose last row ends
     // inside a dword would lose its last element: round the range up to 16
@@ -128,15 +138,25 @@ struct OperandLoader {
     // element's 16-byte block (and page) and only feed discarded columns.
     int64_t left = (bytes_left - step + 15) & ~(int64_t)15;
     left = left < 0 ? 0 : (left > 0x7FFFFFF0 ? 0x7FFFFFF0 : left);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(tile_base + step, (uint32_t)left);
-    // Valid K in this stage (clamped: only "less than kBK or not" matters).
     const int64_t krem64 = K - (int64_t)kt * kBK;
-    const int krem = krem64 > kBK ? kBK : (int)krem64;
+    *krem = krem64 > kBK ? kBK : (int)krem64;
+    return make_rsrc(tile_base + step, (uint32_t)left);
+  }
+
+  // Load j (0..3) of this wave's 4 loads of a stage, from the stage's
+  // resource `r` into the stage slot at LDS offset `slot`.  A stage past
+  // the end of K (empty resource) still issues its loads: they fall out of
+  // range and write zeros, which keeps the count of loads per iteration
+  // fixed; the slot they fill holds no live stage.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
+                                       int j) const {
+    dma16(r, lds_at(slot + (wave * 4 + j) * 1024), (kpos[j] < krem) ? off[j] : kOobOffset);
+  }
+  __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
+    int krem;
+    const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt, K, &krem);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t v = (kpos[j] < krem) ? off[j] : kOobOffset;
-      dma16(r, lds_at(slot * kStageBytes + half + (wave * 4 + j) * 1024), v);
-    }
+    for (int j = 0; j < 4; ++j) load(r, krem, slot, wave, j);
   }
 };
 
@@ -200,28 +220,34 @@ struct FragReader<1, true> {
 // column i of the block.  Rows are K and columns are M or N here, so each
 // lane receives 4 consecutive k of its own column: lane l gets column l % 32
 // of the block and k = 8 (l / 32) + 0..3 (first read) and + 4..7 (second).
+// A 32-column block is one half of a 64-column panel; the swizzle flips
+// which half depending on k, so even and odd blocks need one lane offset
+// each.
 template <>
 struct FragReader<2, false> {
   typedef bf16x8 frag_t;
   static constexpr int kSteps = 2;
   static constexpr int kReads = 2;
-  static constexpr int kRowBytes = 64;  // one K row of a panel
-  uint32_t off;
+  uint32_t off[2];  // for even and odd blocks
   __device__ __forceinline__ void init(int col0, int lane) {
     const int g = lane >> 4, t = lane & 15;
-    const int n = 16 * (g & 1) + 4 * (t & 3);  // column within the panel
     const int k = 8 * (g >> 1) + (t >> 2);
-    off = (col0 / 32) * kPanelBytes + k * kRowBytes + n * 2;
+    const int chunk = 2 * (g & 1) + ((t & 3) >> 1);  // 16-byte chunk within the block's half
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      off[b] = (col0 / 64) * Panel<2>::kBytes + k * kPanelRowBytes +
+               (((4 * b + chunk) ^ swz_mn<2>(k)) << 4) + 8 * (t & 1);
   }
   template <int BLK, int KS>
   __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
-    constexpr uint32_t c = BLK * kPanelBytes + 16 * KS * kRowBytes;
+    // k + 16 KS and k + 4 keep swz_mn, so both are constant offsets.
+    constexpr uint32_t c = (BLK >> 1) * Panel<2>::kBytes + 16 * KS * kPanelRowBytes;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off + c));
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off + c + 4 * kRowBytes));
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c + 4 * kPanelRowBytes));
     const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(frag_t, v);
   }
@@ -231,27 +257,31 @@ struct FragReader<2, false> {
 // group of 16 lanes the instruction reads an 8 x 16 block of bytes (lanes 2r
 // and 2r+1 fetch the two halves of row r) and hands lane i column i, i.e. 8
 // consecutive k of its own column: lane l gets column l % 32 of the block and
-// k = 32 (l / 32) + 8 h + 0..7 from read h.
+// k = 32 (l / 32) + 8 h + 0..7 from read h.  A 32-column block is one 32-byte
+// piece of a 128-column panel, placed by the swizzle, so each of a wave's
+// four blocks has its own lane offset.
 template <>
 struct FragReader<1, false> {
   typedef i32x8 frag_t;
   static constexpr int kSteps = 1;
   static constexpr int kReads = 4;
-  static constexpr int kRowBytes = 32;
-  uint32_t off;
+  uint32_t off[4];  // per block
   __device__ __forceinline__ void init(int col0, int lane) {
     const int g = lane >> 4, t = lane & 15;
-    const int n = 16 * (g & 1) + 8 * (t & 1);
     const int k = 32 * (g >> 1) + (t >> 1);
-    off = (col0 / 32) * kPanelBytes + k * kRowBytes + n;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      off[b] = (col0 / 128) * Panel<1>::kBytes + k * kPanelRowBytes +
+               (((2 * b + (g & 1)) ^ swz_mn<1>(k)) << 4) + 8 * (t & 1);
   }
   template <int BLK, int KS>
   __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
     i32x8 v;
+    // k + 8 h keeps swz_mn, so the four reads are constant offsets apart.
     static_for<0, 4>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
       const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (MIGEMM_LDS i32x2*)lds_at(opnd_base + off + BLK * kPanelBytes + 8 * h * kRowBytes));
+          (MIGEMM_LDS i32x2*)lds_at(opnd_base + off[BLK] + 8 * h * kPanelRowBytes));
       v[2 * h] = w[0];
       v[2 * h + 1] = w[1];
     });
@@ -282,12 +312,12 @@ struct Accum {
 // The fragments one wave needs from one stage, in two halves of 32 VGPRs so
 // that one half can be refilled while the MFMAs of the other run.
 //   bf16:  half h = the 4 A and 4 B fragments of k-step h (16 bytes each);
+//          phase 0 = the 16 MFMAs of half 0, phase 1 = those of half 1.
 //   e4m3:  half h = A fragments {2h, 2h+1} and B fragments {2h, 2h+1}
-//          (32 bytes each; the stage is a single k-step).
-// MFMA (i, j) -- 32-row block i of A with 32-column block j of B -- runs in
-//   phase 0: it needs half 0 only       (bf16: k-step 0; e4m3: i<2, j<2)
-//   phase 1: it needs both halves       (bf16: none;     e4m3: the mixed ones)
-//   phase 2: it needs half 1 only       (bf16: k-step 1; e4m3: i>=2, j>=2)
+//          (32 bytes each; the stage is a single k-step); MFMA (i, j) needs
+//          A half i/2 and B half j/2, and the four phases are
+//            phase 0: A0 B0,  phase 1: A1 B0,  phase 2: A0 B1,  phase 3: A1 B1,
+//          so B half 0 is free after phase 1 and A half 0 after phase 2.
 template <int ES, bool AK, bool BK>
 struct FragHalves {
   typedef FragReader<ES, AK> RA;
@@ -299,11 +329,8 @@ struct FragHalves {
   RA ra;
   RB rb;
 
-  // LDS read instructions of one half, and MFMAs of each phase.
+  // LDS read instructions of one half.
   static constexpr int kReadInsts = kPerHalf * (RA::kReads + RB::kReads);
-  static constexpr int kPhase0 = kBf16 ? 16 : 4;
-  static constexpr int kPhase1 = kBf16 ? 0 : 8;
-  static constexpr int kPhase2 = kBf16 ? 16 : 4;
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     ra.init(wm * kWaveTile, lane);
@@ -311,18 +338,17 @@ struct FragHalves {
   }
 
   // Fragments [Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ) of half H from
-  // ring slot `slot`.
-  template <int H, int Q, int NQ>
-  __device__ __forceinline__ void read_part(int slot) {
-    const uint32_t a_base = slot * kStageBytes;
-    const uint32_t b_base = a_base + kOperandStageBytes;
+  // the stage slots at LDS offsets a_base (A) and b_base (B).
+  // OPS: 1 = A only, 2 = B only, 3 = both.
+  template <int H, int Q, int NQ, int OPS = 3>
+  __device__ __forceinline__ void read_part(uint32_t a_base, uint32_t b_base) {
     static_for<Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ>([&](auto xc) {
       constexpr int x = decltype(xc)::value;
       // bf16: block x of k-step H; e4m3: block 2H + x of the single k-step
       constexpr int blk = kBf16 ? x : 2 * H + x;
       constexpr int ks = kBf16 ? H : 0;
-      a[H][x] = ra.template read<blk, ks>(a_base);
-      b[H][x] = rb.template read<blk, ks>(b_base);
+      if constexpr ((OPS & 1) != 0) a[H][x] = ra.template read<blk, ks>(a_base);
+      if constexpr ((OPS & 2) != 0) b[H][x] = rb.template read<blk, ks>(b_base);
     });
   }
 
@@ -333,14 +359,13 @@ struct FragHalves {
     static_for<FIRST, FIRST + COUNT>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       if constexpr (kBf16) {
-        constexpr int h = P == 0 ? 0 : 1;  // phase 1 is empty for bf16
+        constexpr int h = P;
         constexpr int i = m >> 2, j = m & 3;
         acc.v[i][j] = mfma<ES>(b[h][j], a[h][i], acc.v[i][j]);
       } else {
-        constexpr int i = P == 0 ? (m >> 1) : P == 2 ? 2 + (m >> 1)
-                                            : (m < 4 ? (m >> 1) : 2 + ((m - 4) >> 1));
-        constexpr int j = P == 0 ? (m & 1) : P == 2 ? 2 + (m & 1) : (m < 4 ? 2 + (m & 1) : (m & 1));
-        acc.v[i][j] = mfma<ES>(b[j >> 1][j & 1], a[i >> 1][i & 1], acc.v[i][j]);
+        constexpr int ha = P & 1, hb = P >> 1;  // A and B half of this phase
+        constexpr int i = 2 * ha + (m >> 1), j = 2 * hb + (m & 1);
+        acc.v[i][j] = mfma<ES>(b[hb][m & 1], a[ha][m >> 1], acc.v[i][j]);
       }
     });
   }
@@ -358,18 +383,6 @@ __device__ __forceinline__ void interleave_mfma_reads() {
   }
 }
 
-// Wait until no more than `pending` stages of this wave's loads are in
-// flight (each stage is 8 vector-memory ops per wave: 4 for A, 4 for B).
-__device__ __forceinline__ void wait_stages_in_flight(int pending) {
-  if (pending >= 2) {
-    wait_vmcnt<16>();
-  } else if (pending == 1) {  // (pending <= 0: wait for everything)
-    wait_vmcnt<8>();
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 // Keeps the compiler from moving any instruction across this point, so the
 // phases of the K loop stay in the order written.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -377,40 +390,49 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // Work that rides along in the K loop: step() is called once per iteration,
 // right after the barrier.
 struct NoSideWork {
-  __device__ __forceinline__ void step(const KernelArgs&, int, int, bool) {}
+  __device__ __forceinline__ void step(const KernelArgs&, int, int, int) {}
 };
 
 // The whole K loop of one output tile.
 //
 // Iteration kt works on stage kt, whose half-0 fragments were read during the
-// previous iteration.  The workgroup barrier certifies stage kt+1 (one ahead):
-//   phase 0: MFMAs on half 0, under which half 1 of stage kt is read; the B
-//            loads of stage kt+2 go out one per 4 MFMAs (bf16);
-//   phase 1: MFMAs needing both halves (e4m3 only), with those B loads;
-//   sync:    wait for this wave's loads of stage kt+1, barrier -- now stage
-//            kt+1 is in LDS for every wave, and every wave is done reading
-//            stage kt-1;
-//   phase 2: the side work steps once; MFMAs on half 1, with the A loads of
-//            stage kt+3 one per 4 MFMAs (e4m3: one per MFMA) and half 0 of
-//            stage kt+1 read under them.
-// Each stage's loads are thus spread over two iterations instead of leaving
-// in one burst after the barrier, when all four waves would queue 32 of them
-// on the CU's address unit at once and starve the MFMA pipe.  Stage s's A
-// half leaves in iteration s-3 (after barrier s-3 freed stage s-4's slot) and
-// its B half in iteration s-2; both are certified in iteration s-1.
+// previous iteration.  The workgroup barrier in the middle certifies stage
+// kt+1 (one ahead):
+//   before:  MFMAs on what is already in registers, under which the rest of
+//            stage kt is read (bf16: half 0's 16 MFMAs with half 1 read in
+//            their first half; e4m3: A0B0 with the half-1 reads, then A1B0);
+//   sync:    wait until only the previous iteration's 8 loads are in flight
+//            -- those of stage kt+2 -- so this wave's loads of stage kt+1 have
+//            landed; barrier: now stage kt+1 is in LDS for every wave, and
+//            every wave is done reading stage kt-1;
+//   after:   the side work steps once; the MFMAs that remain (bf16: half 1;
+//            e4m3: A0B1, A1B1), the first four each followed by two of the 8
+//            loads of stage kt+3 (into stage kt-1's slot), the next ones
+//            with stage kt+1's half-0 reads.
+// Fragment reads are issued early in their phase so that they have landed
+// before anything waits for them (the compiler waits for every LDS read at
+// the top of the loop).  Each stage gets two iterations to land.  Loads of
+// stages past K fall out of range and only zero a free slot, so every
+// iteration issues exactly 8 loads per wave.  (Spreading a stage's loads
+// over two iterations was measured to be slower: it costs more in latency
+// budget than it gains in issue smoothness.)
 template <int ES, bool AK, bool BK, class SideWork>
 __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn, int wave,
                                          int lane, SideWork& side) {
   static_assert(kStages == 4, "the certify-ahead ring is written for 4 stages");
   typedef FragHalves<ES, AK, BK> FH;
   constexpr int kBK = kStageKBytes / ES;
+  constexpr uint32_t kB = kOperandStageBytes;
   OperandLoader<ES, AK> la;
   OperandLoader<ES, BK> lb;
   la.init(a.A, a.a_bytes, a.lda, (int64_t)tm * kTileM, wave, lane);
   lb.init(a.B, a.b_bytes, a.ldb, (int64_t)tn * kTileN, wave, lane);
   const int wm = wave >> 1, wn = wave & 1;
-  const int KT = (int)((a.K + kBK - 1) / kBK);
-  constexpr int kB = kOperandStageBytes;
+  int KT = (int)((a.K + kBK - 1) / kBK);
+  // Opaque per tile, like the lane ids: tests on KT are then made where they
+  // are used, not once before the tile loop and held (or spilled, and
+  // reloaded with a vmcnt(0)) across it.
+  asm volatile("" : "+s"(KT));
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -421,78 +443,97 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   f.init(wm, wn, lane);
   if (KT > 0) {
     // Prologue: stages 0..2 in flight, stage 0 certified, its half 0 read.
-    for (int s = 0; s < kStages - 1 && s < KT; ++s) {
-      la.issue(s, s, 0, a.K, wave);
-      lb.issue(s, s, kB, a.K, wave);
+    for (int s = 0; s < kStages - 1; ++s) {
+      la.load_all(s, s * kStageBytes, a.K, wave);
+      lb.load_all(s, s * kStageBytes + kB, a.K, wave);
     }
-    wait_stages_in_flight(min(kStages - 2, KT - 1));
+    wait_vmcnt<16>();
     barrier();
-    f.template read_part<0, 0, 1>(0);
+    f.template read_part<0, 0, 1>(0, kB);
   }
   for (int kt = 0; kt < KT; ++kt) {
     // Every iteration has the same shape (no branch around MFMAs, so the
     // accumulators never meet at a join): in the last ones the barrier is
     // redundant and the half-0 read fetches bytes nobody uses.
-    const int slot = kt % kStages;
-    const int sb = kt + 2;                       // stage whose B half leaves now
-    const bool b_due = kt >= 1 && sb < KT;       // (stage 2's left in the prologue)
-    const int sa = kt + 3;                       // stage whose A half leaves now
-    const bool a_due = sa < KT;
-    const int nslot = (kt + 1) % kStages;
+    const uint32_t cur = (kt % kStages) * kStageBytes;
+    const uint32_t nxt = ((kt + 1) % kStages) * kStageBytes;
+    const uint32_t s3 = ((kt + 3) % kStages) * kStageBytes;
+    int krem_a, krem_b;
+    const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(kt + 3, a.K, &krem_a);
+    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(kt + 3, a.K, &krem_b);
+    // The stage-(kt+3) load that follows MFMA q (0..3) of the after-barrier
+    // part: two per MFMA, A first.
+    auto loads_after = [&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      if constexpr (q < 2) {
+        la.load(ra, krem_a, s3, wave, 2 * q);
+        la.load(ra, krem_a, s3, wave, 2 * q + 1);
+      } else {
+        lb.load(rb, krem_b, s3 + kB, wave, 2 * q - 4);
+        lb.load(rb, krem_b, s3 + kB, wave, 2 * q - 3);
+      }
+    };
     if constexpr (FH::kBf16) {
-      static_for<0, 4>([&](auto qc) {
+      static_for<0, 2>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         sched_fence();
-        if (b_due) lb.issue_one(sb, sb % kStages, kB, a.K, wave, q);
-        f.template read_part<1, q, 4>(slot);
+        f.template read_part<1, q, 2>(cur, cur + kB);
         f.template mma<0, 4 * q, 4>(acc);
-        interleave_mfma_reads<4, FH::kReadInsts / 4>();
+        interleave_mfma_reads<4, FH::kReadInsts / 2>();
       });
+      sched_fence();
+      f.template mma<0, 8, 8>(acc);
     } else {
       sched_fence();
-      f.template read_part<1, 0, 1>(slot);
-      f.template mma<0, 0, FH::kPhase0>(acc);
-      interleave_mfma_reads<FH::kPhase0, FH::kReadInsts>();
-      static_for<0, 4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        if (b_due) lb.issue_one(sb, sb % kStages, kB, a.K, wave, q);
-        f.template mma<1, 2 * q, 2>(acc);
-      });
+      f.template read_part<1, 0, 1, 1>(cur, cur + kB);  // A half 1 first: phase 1 needs it
+      f.template read_part<1, 0, 1, 2>(cur, cur + kB);
+      f.template mma<0, 0, 4>(acc);
+      interleave_mfma_reads<4, FH::kReadInsts>();
+      sched_fence();
+      f.template mma<1, 0, 4>(acc);
     }
     sched_fence();
-    // Stage kt+1's last loads (its B half) left in iteration kt-1, or in the
-    // prologue; younger than them are at most the 8 loads of stage kt+2, which
-    // may stay in flight.  Any other vector memory operation issued after
-    // them only makes this wait stricter: vector memory operations complete
-    // in order.
-    wait_stages_in_flight(min(KT - 2 - kt, 1));
+    wait_vmcnt<8>();
     barrier();
-    // Since the side work's previous step, this wave has issued exactly the
-    // 8 stage loads of stage kt+2 (if that stage exists).
-    side.step(a, wave, lane, kt + 2 < KT);
+    // The side work's previous fetch left just before the previous
+    // iteration's 8 loads, so only those are younger than it.
+    side.step(a, wave, lane, 8);
     if constexpr (FH::kBf16) {
       static_for<0, 4>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         sched_fence();
-        if (a_due) la.issue_one(sa, sa % kStages, 0, a.K, wave, q);
-        f.template read_part<0, q, 4>(nslot);
-        f.template mma<2, 4 * q, 4>(acc);
-        interleave_mfma_reads<4, FH::kReadInsts / 4>();
+        f.template mma<1, q, 1>(acc);
+        loads_after(qc);
       });
+      static_for<0, 2>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        f.template read_part<0, q, 2>(nxt, nxt + kB);
+        f.template mma<1, 4 + 4 * q, 4>(acc);
+        interleave_mfma_reads<4, FH::kReadInsts / 2>();
+      });
+      sched_fence();
+      f.template mma<1, 12, 4>(acc);
     } else {
+      // A0B1 (B half 0 is free now): the loads, then B half 0 of stage kt+1.
       static_for<0, 4>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         sched_fence();
-        if (a_due) la.issue_one(sa, sa % kStages, 0, a.K, wave, q);
-        f.template read_part<0, q, 4>(nslot);
         f.template mma<2, q, 1>(acc);
-        interleave_mfma_reads<1, FH::kReadInsts / 2>();
+        loads_after(qc);
       });
+      sched_fence();
+      f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
+      // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first.
+      sched_fence();
+      f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
+      f.template mma<3, 0, 4>(acc);
     }
   }
-  // Every wave is done with the ring before anyone reuses it.
+  // Every wave is done with the ring, and every load into it (including the
+  // zero-filling ones past K) has landed, before anyone reuses it.
   sched_fence();
+  wait_vmcnt<0>();
   wait_lgkmcnt<0>();
   barrier();
 }

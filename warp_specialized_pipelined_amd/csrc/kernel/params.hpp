@@ -14,33 +14,36 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveTile = 128;
 // Each main-loop stage holds 64 bytes of K for every row of the A and B
-// tiles (32 bf16 or 64 e4m3 values): 16 KiB of A + 16 KiB of B.
+// tiles (32 bf16 or 64 e4m3 values): 16 KiB of A + 16 KiB of B.  Stage s
+// lives in slot s % kStages of the LDS ring.
 constexpr int kStageKBytes = 64;
 constexpr int kOperandStageBytes = kTileM * kStageKBytes;  // 16 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;        // 32 KiB
 constexpr int kStages = 4;                                 // LDS ring depth
 constexpr int kRingBytes = kStages * kStageBytes;          // 128 KiB
+constexpr int kLdsLimit = 160 * 1024;                      // LDS per workgroup on gfx950
 // Epilogue staging: each wave's 128 x 128 bf16 quarter of the tile, rows
 // padded from 256 to 272 bytes so that consecutive rows start 4 banks apart.
 // It overlays the (then idle) ring and runs a little past it.
 constexpr int kStagingRowBytes = kWaveTile * 2 + 16;                 // 272
 constexpr int kStagingWaveBytes = kWaveTile * kStagingRowBytes;      // 34816
 constexpr int kStagingBytes = kWaves * kStagingWaveBytes;            // 139264
+constexpr int kPlainLdsBytes = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
 // Consumer-stage landing slots: per wave kConsumerDepth slots of 1 KiB (16
 // bytes per lane), past both the ring and the staging area.  The consumer
 // fetches while the K loop runs (so the slots must not overlap the ring),
 // and one wave may still be draining its consumer work while another
 // already stages its epilogue (so they must not overlap the staging either).
 constexpr int kConsumerDepth = 4;
-constexpr int kConsumerSlotOffset = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
+constexpr int kConsumerSlotOffset = kPlainLdsBytes;
 constexpr int kConsumerSlotBytes = 64 * 16;
 constexpr int kConsumerEnd = kConsumerSlotOffset + kWaves * kConsumerDepth * kConsumerSlotBytes;
 // Tile hand-off ring: two slots of {tile id, full count, empty count}.
 constexpr int kHandoffSlots = 2;
 constexpr int kHandoffOffset = kConsumerEnd;
 constexpr int kHandoffBytes = 64;
-constexpr int kLdsBytes = kHandoffOffset + kHandoffBytes;
-static_assert(kLdsBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+constexpr int kConsumerLdsBytes = kHandoffOffset + kHandoffBytes;     // 155712
+static_assert(kConsumerLdsBytes <= kLdsLimit, "consumer kernel LDS exceeds 160 KiB");
 
 struct KernelArgs {
   const void* A;       // operand storage (after any swap of A and B)

@@ -15,6 +15,9 @@ struct KernelSelect {
   bool consumer;    // tile hand-off + consumer stage
 };
 
+// Dynamic LDS the selected kernel uses.
+int kernel_lds_bytes(const KernelSelect& sel);
+
 // Raise the kernel's dynamic-LDS limit to what it uses (once per process).
 hipError_t prepare_kernel(const KernelSelect& sel);
 
