@@ -158,8 +158,10 @@ def gemm_entries(M, N, K, A: Operand, B: Operand, C: Operand | None, alpha: floa
 
 
 def tile_rowstats(D_codes: np.ndarray, M: int, N: int, d_rs: int, d_cs: int, tile_n: int = 256):
-    """Sequential fp32 row sums and maxNum row maxima per tile_n-wide slice of a
-    bf16 D.  Returns (row_sum, row_max), float32 [M, ceil(N/tile_n)]."""
+    """Row sums and row maxima per tile_n-wide slice of a bf16 D, in the
+    order orc_tile_rowstats states (8-column sequential chunk sums, then a
+    balanced binary tree over the chunks; max ignoring NaN with -0 < +0).
+    Returns (row_sum, row_max), float32 [M, ceil(N/tile_n)]."""
     lib = _load()
     D_codes = np.ascontiguousarray(D_codes).reshape(-1).view(np.uint16)
     ld = (N + tile_n - 1) // tile_n

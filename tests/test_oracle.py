@@ -357,20 +357,58 @@ def bf16_codes(vals):
     return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def test_rowstats_sum_is_sequential_fp32():
-    row = [1.0] + [2.0 ** -24] * 255          # each addition rounds back to 1.0
-    D = bf16_codes([row])
-    s, m = oracle.tile_rowstats(D, 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(1.0)
-    assert m[0, 0] == np.float32(1.0)
-    # the pairwise (tree) sum would keep the small terms
-    assert float(np.sum(np.array(row, dtype=np.float32))) != 1.0
-    row = [2.0 ** 24] + [1.0] * 255           # 2^24 + 1 rounds to 2^24 (ties to even)
+def chunks_row(chunk_vals, n_chunks=32):
+    """A 256-column row whose chunk k (8 columns) holds eight copies of
+    chunk_vals.get(k, 0)."""
+    row = []
+    for k in range(n_chunks):
+        row += [chunk_vals.get(k, 0.0)] * 8
+    return row
+
+
+def test_rowstats_sum_order():
+    # all ones: 256 in any order
+    s, m = oracle.tile_rowstats(bf16_codes([[1.0] * 256]), 1, 256, 256, 1, 256)
+    assert s[0, 0] == np.float32(256.0) and m[0, 0] == np.float32(1.0)
+    # chunk 0 = [2^24, 1 x 7]: summed in column order inside the chunk, each
+    # +1 rounds back to 2^24 (ties to even); the other 31 chunks are 8 each and
+    # reach the total exactly: 2^24 + 248.  (A plain column-order sum would
+    # give 2^24; a tree inside the chunk would keep 6 of the 7 ones.)
+    row = [2.0 ** 24] + [1.0] * 255
+    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
+    assert s[0, 0] == np.float32(2.0 ** 24 + 248)
+    # chunk 0 = [1 x 7, 2^24]: 7 + 2^24 rounds to 2^24 + 8, then + 248.
+    row = [1.0] * 7 + [2.0 ** 24] + [1.0] * 248
+    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
+    assert s[0, 0] == np.float32(2.0 ** 24 + 256)
+    # adjacent chunks pair first: c0 = 2^24 (8 x 2^21), c1 = c17 = 1 (8 x 1/8).
+    # c0 + c1 loses its 1 before c17's 1 arrives, so the total is 2^24; pairing
+    # chunk i with chunk i+16 would add 1 + 1 first and give 2^24 + 2.
+    row = chunks_row({0: 2.0 ** 21, 1: 0.125, 17: 0.125})
     s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
     assert s[0, 0] == np.float32(2.0 ** 24)
-    row = [1.0] * 255 + [2.0 ** 24]           # order matters: 255 + 2^24 is exact
-    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(2.0 ** 24 + 255)
+    # signed zeros: a full slice of -0 sums to -0; a slice cut short by N is
+    # padded with +0, and -0 + +0 = +0.
+    s, m = oracle.tile_rowstats(bf16_codes([[-0.0] * 256]), 1, 256, 256, 1, 256)
+    assert s.view(np.uint32)[0, 0] == 0x80000000 and m.view(np.uint32)[0, 0] == 0x80000000
+    s, _ = oracle.tile_rowstats(bf16_codes([[-0.0] * 300]), 1, 300, 300, 1, 256)
+    assert s.view(np.uint32)[0, 1] == 0x00000000
+
+
+def test_rowstats_max_rules():
+    def rmax(vals):
+        _, m = oracle.tile_rowstats(bf16_codes([vals]), 1, len(vals), len(vals), 1, 256)
+        return m[0, 0]
+    base = [-3.0] * 256
+    v = list(base); v[200] = 0.0; v[10] = -0.0
+    assert np.float32(rmax(v)).view(np.uint32) == 0x00000000        # +0 beats -0 wherever it is
+    v = list(base); v[10] = 0.0; v[200] = -0.0
+    assert np.float32(rmax(v)).view(np.uint32) == 0x00000000
+    v = list(base); v[5] = float("nan"); v[100] = -1.0
+    assert rmax(v) == np.float32(-1.0)                               # NaN ignored
+    assert rmax([float("nan")] * 256) == np.float32(-np.inf)         # nothing left: -inf
+    v = list(base); v[255] = 2.0 ** 100
+    assert rmax(v) == np.float32(2.0 ** 100)
 
 
 def test_rowstats_slices_and_max():
@@ -385,10 +423,10 @@ def test_rowstats_slices_and_max():
     for r in range(M):
         for t, (lo, hi) in enumerate([(0, 256), (256, 512), (512, 600)]):
             seg = dv[r, lo:hi]
-            acc = np.float32(0.0)
-            for v in seg:
-                acc = np.float32(acc + v)
-            assert s[r, t] == acc
+            # all values are in [-5, -1] or zero and have 8 significant bits,
+            # so every partial sum of up to 256 of them is exact in fp32 and
+            # any order gives the exact sum
+            assert s[r, t] == np.float32(np.sum(seg.astype(np.float64)))
             assert m[r, t] == seg.max()
     assert m[1, 1] == 0.0 and m[2, 2] == 0.0
     # column-major D gives the same statistics

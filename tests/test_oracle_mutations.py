@@ -36,7 +36,12 @@ MUTATIONS = [
      "    if (beta != 0.0) r += beta * elem(c_type, C, c_cs, c_rs, i, j);\n    ref[e] = r;"),
     ("rowsum_in_double", "volatile float s = 0.0f;", "volatile double s = 0.0;"),
     ("rowmax_from_zero", "float m = -INFINITY;", "float m = 0.0f;"),
-    ("rowstats_short_slice", "for (int64_t j = t * tile_n; j < j_end; ++j) {", "for (int64_t j = t * tile_n; j + 1 < j_end; ++j) {"),
+    ("rowstats_short_chunk", "for (int64_t e = 0; e < 8; ++e) {", "for (int64_t e = 0; e < 7; ++e) {"),
+    ("tree_strided_pairs", "volatile float v = c[2 * i] + c[2 * i + 1];", "volatile float v = c[i] + c[i + n / 2];"),
+    ("max_signed_zero_ignored", "return signbit(a) ? b : a;", "return a;"),
+    ("max_keeps_nan", "if (j < N && !isnan(v)) m = max_signed_zero(m, v);", "if (j < N) m = max_signed_zero(m, v);"),
+    ("pad_with_minus_zero", "(float)orc_bf16_value(D[r * d_rs + j * d_cs]) : 0.0f;",
+     "(float)orc_bf16_value(D[r * d_rs + j * d_cs]) : -0.0f;"),
 ]
 
 

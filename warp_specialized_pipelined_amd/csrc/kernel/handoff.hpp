@@ -25,12 +25,15 @@
 // over the first iterations of tile n+1's K loop, one 16-byte chunk per lane
 // per iteration, so it runs in the shadow of the MFMAs.
 //
-// Consumer work for a 256 x 256 tile at tile column t: for each of its rows r
-// (one lane per row),
-//   row_sum[r][t] = fp32 sum, in ascending column order from +0.0f, of the
-//                   bf16 values of D in that row of the tile,
-//   row_max[r][t] = maxNum of the same values, from -inf,
-// and the row is copied bit for bit to D_copy.
+// Consumer work for a 256 x 256 tile at tile column t: for each of its rows r,
+// over the tile's columns (those past N read as +0.0 for the sum and are left
+// out of the max), in an order fixed so that it can be checked bit for bit:
+//   chunk k = columns 8k .. 8k+7:  c_k = (((x0 + x1) + x2) + ...) + x7   (fp32)
+//   row_sum[r][t] = balanced binary tree over c_0 .. c_31, adjacent pairs
+//                   first (c_0 + c_1, c_2 + c_3, ...; then pairs of those, ...)
+//   row_max[r][t] = the largest non-NaN value, with -0 < +0; -inf if none,
+// and the row is copied bit for bit to D_copy.  (The pages leave the
+// consumer's arithmetic open; this order lets 32 lanes share a row.)
 #pragma once
 
 #include "gfx950.hpp"
@@ -84,38 +87,85 @@ struct HandoffRing {
   }
 };
 
-// One lane's share of the consumer work on one tile: one row.
-//
-// The row is read in 16-byte chunks.  Each chunk is fetched with an LDS-DMA
-// load into the lane's 16 bytes of one of its wave's landing slots, then
-// waited for, read back, and folded in.  Going through LDS (like the K-loop
-// ring) keeps every wait explicit: the compiler never sees an outstanding
-// load, so it never answers one with a vmcnt(0) that would also drain the
-// ring.  Inside the K loop one chunk is fetched per iteration, just before
-// the iteration's stage loads, and folded in one iteration later, when only
-// those 8 stage loads are younger than it; after the loop the rest of the
-// row is drained with kConsumerDepth fetches in flight.
-struct TileConsumer {
-  __amdgpu_buffer_rsrc_t rsrc;  // D from the tile's first row and column
-  uint32_t row_off;            // byte offset of this lane's row in rsrc (kOobOffset: no row)
-  unsigned short* dst;         // D_copy row, first column of the tile
-  int64_t stat;                // index of this row's entry in row_sum / row_max
-  int ncols;                   // valid columns of the tile
-  int fetched;                 // chunks fetched so far
-  int done;                    // chunks folded in so far
-  int slot;
-  bool active;
-  bool has_row;
-  float sum, mx;
+// IEEE total order on non-NaN floats as signed integers (-0 < +0), and back.
+__device__ __forceinline__ int32_t order_key(float x) {
+  const int32_t b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_order_key(int32_t k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
 
-  __device__ __forceinline__ int chunks() const { return (ncols + 7) >> 3; }
-  __device__ __forceinline__ void idle() { active = false; }
+// Butterfly partner values within groups of 32 lanes (DPP): pairs at
+// distance 1 and 2 (quad permutes), then the mirror images within 8 and 16
+// lanes -- after the earlier levels every lane of a group holds its group's
+// value, so mirroring pairs the same groups as a distance-4 or -8 exchange.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+// One wave's share of the consumer work on one tile: rows 64w .. 64w+63, two
+// per step.  Step j covers rows 64w + 2j (lanes 0-31) and 64w + 2j + 1 (lanes
+// 32-63); lane l takes the 16 bytes (8 columns) 8 (l % 32) .. + 7 of its row,
+// so every step reads and writes two whole 512-byte rows: the memory
+// pipeline sees 2 long segments per instruction instead of 64 short ones.
+//
+// A step's 16 bytes are fetched with an LDS-DMA load into the lane's slot of
+// one of its wave's landing slots.  Going through LDS (like the K-loop ring)
+// keeps every wait explicit: the compiler never sees an outstanding load, so
+// it never answers one with a vmcnt(0) that would also drain the ring.
+//
+// Inside the K loop a step takes three iterations:
+//   iteration i:   fetch (after the barrier, before the stage loads);
+//   iteration i+1: after its barrier -- whose wait covered the fetch -- read
+//                  the landing slot back; fold the 16 bytes in between the
+//                  MFMAs that follow (compute<0..2>);
+//   iteration i+2: after its barrier, store the copy and the statistics.
+// Stores leave before the iteration's stage loads, so the stage loads stay
+// the youngest 8 vector memory operations at every wait.  After the K loop
+// the rest is finished synchronously (drain).
+struct TileConsumer {
+  static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
+  // Buffer resources from the tile's origin: D (fetch) and D_copy (store)
+  // share their layout, so one offset serves both; the statistics have one
+  // 4-byte entry per row.  Out-of-range offsets read zeros and drop stores,
+  // which is how rows and columns outside the matrix are masked.
+  __amdgpu_buffer_rsrc_t src, cpy, rsum, rmax;
+  uint32_t lane_off;            // byte offset of this lane's 16 bytes in step 0
+  uint32_t step_bytes;          // two rows of D
+  uint32_t stat_off;            // byte offset of this lane's row statistics in step 0
+  uint32_t stat_step;           // two rows of statistics
+  int row0;                     // this lane's row within the tile in step 0
+  int rows;                     // valid rows of the tile
+  int ncols;                    // valid columns of the tile
+  int fetched;                  // steps fetched so far
+  int folded;                   // steps read back (and folded) so far
+  int slot;
+  bool active;                  // steps of this tile remain to be stored
+  // The step being folded in this iteration (folding), and the one whose
+  // results wait for their stores (pending).
+  bool folding, pending;
+  int fold_j, pend_j;
+  u32x4 v;                      // the step's 16 bytes (folding), then its copy (pending)
+  float sum;                    // this lane's chunk sum, then its row's sum
+  int32_t mkey;                 // same for the maximum, as an order key
+
+  __device__ __forceinline__ void idle() {
+    active = false;
+    folding = false;
+    pending = false;
+  }
 
   __device__ __forceinline__ static uint32_t landing(int wave, int c) {
     return kConsumerSlotOffset + (wave * kConsumerDepth + (c % kConsumerDepth)) * kConsumerSlotBytes;
   }
 
-  // Wait for the use-th commit of `slot`, then set up this lane's row.
+  // Wait for the use-th commit of `slot`, then set up this lane's share.
   __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int wave,
                                         int lane) {
     slot = slot_;
@@ -123,92 +173,152 @@ struct TileConsumer {
     const TileCoord t = tile_of(tile_id, a);
     const int64_t r0 = (int64_t)t.tm * kTileM;
     const int64_t c0 = (int64_t)t.tn * kTileN;
-    const int r = wave * 64 + lane;
-    const int64_t left = a.N - c0;
-    ncols = (int)(left < kTileN ? left : kTileN);
-    const unsigned short* base = static_cast<const unsigned short*>(a.D) + r0 * a.ldd + c0;
+    const int64_t rleft = a.M - r0, cleft = a.N - c0;
+    rows = (int)(rleft < kTileM ? rleft : kTileM);
+    ncols = (int)(cleft < kTileN ? cleft : kTileN);
+    row0 = wave * 64 + (lane >> 5);
+    const int col = 8 * (lane & 31);
     int64_t bytes = ((a.M - 1 - r0) * a.ldd + (a.N - c0)) * 2;
-    bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see OperandLoader::issue
-    rsrc = make_rsrc(base, (uint32_t)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes));
-    has_row = r0 + r < a.M;
-    row_off = has_row ? (uint32_t)(r * a.ldd * 2) : kOobOffset;
-    dst = static_cast<unsigned short*>(a.D_copy) + (r0 + r) * a.ldd + c0;
-    stat = (r0 + r) * a.stat_ld + t.tn;
+    bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see OperandLoader::stage_rsrc
+    const uint32_t nb = (uint32_t)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+    src = make_rsrc(static_cast<const unsigned short*>(a.D) + r0 * a.ldd + c0, nb);
+    cpy = make_rsrc(static_cast<const unsigned short*>(a.D_copy) + r0 * a.ldd + c0, nb);
+    const int64_t s0 = r0 * a.stat_ld + t.tn;
+    int64_t sbytes = (a.M * (int64_t)a.stat_ld - s0) * 4;
+    sbytes = sbytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : sbytes;
+    rsum = make_rsrc(a.row_sum + s0, (uint32_t)sbytes);
+    rmax = make_rsrc(a.row_max + s0, (uint32_t)sbytes);
+    lane_off = col < ncols ? (uint32_t)((row0 * a.ldd + col) * 2) : kOobOffset;
+    step_bytes = (uint32_t)(2 * a.ldd * 2);
+    stat_off = (lane & 31) == 0 ? (uint32_t)(row0 * a.stat_ld * 4) : kOobOffset;
+    stat_step = (uint32_t)(2 * a.stat_ld * 4);
     fetched = 0;
-    done = 0;
-    sum = 0.0f;
-    mx = -__builtin_inff();
+    folded = 0;
     active = true;
+    folding = false;
+    pending = false;
+  }
+
+  // This lane's offset (from `base`, per step `step`) for step j, or an
+  // out-of-range one when the step's row is past the tile's last.
+  __device__ __forceinline__ uint32_t at(uint32_t base, uint32_t step, int j) const {
+    return (base != kOobOffset && row0 + 2 * j < rows) ? base + (uint32_t)j * step : kOobOffset;
   }
 
   __device__ __forceinline__ void fetch(int wave) {
-    const int c = fetched++;
-    dma16(rsrc, lds_at(landing(wave, c)), row_off == kOobOffset ? kOobOffset : row_off + 16 * c);
+    const int j = fetched++;
+    dma16(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
   }
 
-  __device__ __forceinline__ void absorb(int c, u32x4 v) {
-    const int col = 8 * c;
-    const int n = ncols - col;
-    if (n >= 8) {
+  // Read step `folded` back from its landing slot (its fetch must have
+  // completed).
+  __device__ __forceinline__ void read_back(int wave, int lane) {
+    compiler_fence();
+    fold_j = folded++;
+    v = *(const MIGEMM_LDS u32x4*)lds_at(landing(wave, fold_j) + 16 * lane);
+    folding = true;
+  }
+
+  // The fold, in three parts: the lane's chunk of 8 columns, the tree over
+  // the 32 lanes of each row, and the row totals.
+  template <int P>
+  __device__ __forceinline__ void compute(int lane) {
+    // Only 32 of a tile's iterations fold a step; the others skip the work
+    // (a uniform branch that jumps over VALU code only, never over MFMAs).
+    if (!folding) return;
+    if constexpr (P == 0) {
+      const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
+      float s = 0.0f;
+      int32_t mk = order_key(-__builtin_inff());
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-        sum = sum + x;
-        mx = fmaxf(mx, x);
+        const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
+        const float x = e < n ? __uint_as_float(h << 16) : 0.0f;
+        s = e == 0 ? x : s + x;
+        if (e < n && x == x) mk = max(mk, order_key(x));
       }
-      *reinterpret_cast<u32x4*>(dst + col) = v;
+      sum = s;
+      mkey = mk;
+    } else if constexpr (P == 1) {
+      // Adjacent chunks first: a balanced tree over the 32 lanes of a row.
+      float s = sum;
+      int32_t mk = mkey;
+      s += __int_as_float(dpp<kDppXor1>(__float_as_int(s)));
+      mk = max(mk, dpp<kDppXor1>(mk));
+      s += __int_as_float(dpp<kDppXor2>(__float_as_int(s)));
+      mk = max(mk, dpp<kDppXor2>(mk));
+      s += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(s)));
+      mk = max(mk, dpp<kDppHalfMirror>(mk));
+      s += __int_as_float(dpp<kDppMirror>(__float_as_int(s)));
+      mk = max(mk, dpp<kDppMirror>(mk));
+      sum = s;
+      mkey = mk;
     } else {
-      for (int e = 0; e < n; ++e) {
-        const uint32_t h = v[e >> 1] >> (16 * (e & 1));
-        const float x = __uint_as_float(h << 16);
-        sum = sum + x;
-        mx = fmaxf(mx, x);
-        dst[col + e] = (unsigned short)h;
-      }
+      // Lanes 0-15 and 16-31 hold the two halves of the first row, lanes
+      // 32-47 and 48-63 those of the second.
+      const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 0));
+      const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 16));
+      const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 32));
+      const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 48));
+      const int32_t m01 = max(__builtin_amdgcn_readlane(mkey, 0), __builtin_amdgcn_readlane(mkey, 16));
+      const int32_t m23 = max(__builtin_amdgcn_readlane(mkey, 32), __builtin_amdgcn_readlane(mkey, 48));
+      const bool second = (lane & 32) != 0;
+      sum = second ? s2 + s3 : s0 + s1;
+      mkey = second ? m23 : m01;
+      folding = false;
+      pending = true;
+      pend_j = fold_j;
     }
   }
 
-  // Fold in the oldest fetched chunk (its fetch must have completed).
-  __device__ __forceinline__ void fold(const KernelArgs& a, int wave, int lane) {
-    compiler_fence();
-    const int c = done++;
-    const u32x4 v = *(const MIGEMM_LDS u32x4*)lds_at(landing(wave, c) + 16 * lane);
-    if (has_row) absorb(c, v);
-    wait_lgkmcnt<0>();  // the read is done before the landing slot is refilled
-    if (done == chunks()) {
-      if (has_row) {
-        a.row_sum[stat] = sum;
-        a.row_max[stat] = mx;
-      }
+  // Store the pending step's copy and statistics; release the slot after the
+  // tile's last step.
+  __device__ __forceinline__ void store_pending(int lane) {
+    if (!pending) return;
+    pending = false;
+    const int j = pend_j;
+    const uint32_t o = at(lane_off, step_bytes, j);
+    if (ncols == kTileN) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, 0);
+    } else {
+      // A tile cut short by N: column by column, past-N ones out of range.
+      const int n = ncols - 8 * (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), cpy,
+                                              e < n ? o + 2 * e : kOobOffset, 0, 0);
+    }
+    const uint32_t so = at(stat_off, stat_step, j);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rsum, so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_order_key(mkey)), rmax, so, 0, 0);
+    if (j == kSteps - 1) {
       active = false;
+      // The tile's reads all completed before their values were folded.
       HandoffRing::release(slot, lane);
     }
   }
 
-  // K-loop hook, once per iteration: fold in the chunk fetched one iteration
-  // earlier, then fetch the next.  Since that fetch the wave has issued the
-  // `since` (8) stage loads of one iteration, all younger than it; vector
-  // memory operations complete in order, so vmcnt(8) covers the fetch
-  // without forcing those stage loads to land.
-  __device__ __forceinline__ void step(const KernelArgs& a, int wave, int lane, int since) {
+  // K-loop hook, right after the barrier.
+  __device__ __forceinline__ void after_barrier(const KernelArgs& a, int wave, int lane) {
+    (void)a;
+    store_pending(lane);
     if (!active) return;
-    if (fetched > done) {
-      if (since >= 8) {
-        wait_vmcnt<8>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      fold(a, wave, lane);
-    }
-    if (active && fetched < chunks()) fetch(wave);
+    if (fetched > folded) read_back(wave, lane);
+    if (fetched < kSteps) fetch(wave);
   }
 
-  // After the K loop: finish the row with up to kConsumerDepth fetches in
+  // After the K loop: finish the tile with up to kConsumerDepth fetches in
   // flight.  newer = fetches issued after the one being waited for.
   __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
+    if (folding) {  // (a K loop always runs its compute parts; kept for safety)
+      compute<0>(lane);
+      compute<1>(lane);
+      compute<2>(lane);
+    }
+    store_pending(lane);
     while (active) {
-      while (fetched < chunks() && fetched - done < kConsumerDepth) fetch(wave);
-      const int newer = fetched - done - 1;
+      while (fetched < kSteps && fetched - folded < kConsumerDepth) fetch(wave);
+      const int newer = fetched - folded - 1;
       static_assert(kConsumerDepth <= 4, "drain waits are written for up to 4 fetches in flight");
       if (newer >= 3) {
         wait_vmcnt<3>();
@@ -219,7 +329,12 @@ struct TileConsumer {
       } else {
         wait_vmcnt<0>();
       }
-      fold(a, wave, lane);
+      read_back(wave, lane);
+      wait_lgkmcnt<0>();  // the read is done before the slot is refilled
+      compute<0>(lane);
+      compute<1>(lane);
+      compute<2>(lane);
+      store_pending(lane);
     }
   }
 };

@@ -387,10 +387,15 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // phases of the K loop stay in the order written.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Work that rides along in the K loop: step() is called once per iteration,
-// right after the barrier.
+// Work that rides along in the K loop.  Once per iteration, right after the
+// barrier (before the iteration's stage loads), after_barrier() issues what
+// the work needs from memory; its arithmetic comes in pieces,
+// compute<P>() for P = 0 .. 2, placed between the MFMAs that follow, so that
+// it fills issue slots instead of holding the MFMA pipe.
 struct NoSideWork {
-  __device__ __forceinline__ void step(const KernelArgs&, int, int, int) {}
+  __device__ __forceinline__ void after_barrier(const KernelArgs&, int, int) {}
+  template <int P>
+  __device__ __forceinline__ void compute(int) {}
 };
 
 // The whole K loop of one output tile.
@@ -495,9 +500,9 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     sched_fence();
     wait_vmcnt<8>();
     barrier();
-    // The side work's previous fetch left just before the previous
-    // iteration's 8 loads, so only those are younger than it.
-    side.step(a, wave, lane, 8);
+    // Anything the side work fetched in the previous iteration left just
+    // before that iteration's 8 loads, so the wait above covered it.
+    side.after_barrier(a, wave, lane);
     if constexpr (FH::kBf16) {
       static_for<0, 4>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
@@ -510,10 +515,12 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
         sched_fence();
         f.template read_part<0, q, 2>(nxt, nxt + kB);
         f.template mma<1, 4 + 4 * q, 4>(acc);
+        side.template compute<q>(lane);
         interleave_mfma_reads<4, FH::kReadInsts / 2>();
       });
       sched_fence();
       f.template mma<1, 12, 4>(acc);
+      side.template compute<2>(lane);
     } else {
       // A0B1 (B half 0 is free now): the loads, then B half 0 of stage kt+1.
       static_for<0, 4>([&](auto qc) {
@@ -524,10 +531,15 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
       });
       sched_fence();
       f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
+      side.template compute<0>(lane);
       // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first.
       sched_fence();
       f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
-      f.template mma<3, 0, 4>(acc);
+      f.template mma<3, 0, 2>(acc);
+      side.template compute<1>(lane);
+      sched_fence();
+      f.template mma<3, 2, 2>(acc);
+      side.template compute<2>(lane);
     }
   }
   // Every wave is done with the ring, and every load into it (including the
