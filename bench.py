@@ -32,6 +32,45 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "traffic_gemm_consumer_bf16_8192.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha1 over the device-side sources (the kernel translation unit and its
+    headers), in a fixed order: identifies the kernel whose counters a
+    traffic profile holds."""
+    import hashlib
+    csrc = os.path.join(HERE, "warp_specialized_pipelined_amd", "csrc")
+    files = [os.path.join(csrc, "gemm_kernels.hip"), os.path.join(csrc, "launch.h")]
+    kdir = os.path.join(csrc, "kernel")
+    files += [os.path.join(kdir, f) for f in sorted(os.listdir(kdir)) if f.endswith(".hpp")]
+    h = hashlib.sha1()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter profile, or None if there is none or the kernel has
+    changed since it was taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha1") != kernel_source_hash():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,7 +273,7 @@ def main():
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "extra": extra,
     }
