@@ -74,8 +74,9 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first: a fresh process needs ~30 to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain/fp8 side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
