@@ -51,9 +51,17 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // explicit vmcnt waits and barriers.  Hidden loads only make the compiler's
 // own vmcnt waits stricter, never looser, because vector memory operations
 // complete in order.
+//
+// The compiler's hazard pass does not look inside inline assembly, so the
+// wait states the gfx9 family requires before this instruction are part of
+// it: 5 after a VALU write of an SGPR the load reads (the resource comes back
+// from a spill lane with v_readlane when SGPRs run short -- without the wait
+// the load can take a half-updated descriptor), and 1 after the SALU write of
+// M0 that the "{m0}" operand puts right in front of it.  s_nop 4 covers both.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r), "{m0}"(m0)
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+               "{m0}"(m0)
                : "memory");
 }
 
