@@ -75,15 +75,16 @@ def check_load(lines, i):
 
 
 def test_lds_dma_loads_have_their_wait_states(kernels):
-    n_loads = 0
     bad = []
     for name, lines in kernels.items():
+        n_loads = 0
         for i, line in enumerate(lines):
             if LDS_LOAD.match(line):
                 n_loads += 1
                 for p in check_load(lines, i):
                     bad.append("%s line %d: %s" % (name[:60], i, p))
-    assert n_loads > 16 * 40, n_loads
+        # every kernel has a K-loop prologue and loop body full of them
+        assert n_loads >= 24, (name, n_loads)
     assert not bad, "\n".join(bad[:20])
 
 

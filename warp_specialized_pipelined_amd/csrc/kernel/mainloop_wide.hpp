@@ -13,12 +13,13 @@
 // With 2 slots, stage d+2 can only be loaded once every wave is done reading
 // stage d.  The last k-step's fragments are read under the third k-step's
 // MFMAs, so the barrier can sit after 48 of the stage's 64 MFMAs, once those
-// reads have returned; the 16 MFMAs of the last k-step run after it, one of
-// the 16 loads of stage d+2 behind each, with the first k-step of stage d+1
-// (certified by the same barrier) read under them.  Loads get 48 MFMAs to
-// land.  Measured against a barrier after 56 MFMAs with two loads behind
-// each of the last 8: the loads spread over twice as many MFMAs keep the
-// address path from bunching up, 4% more throughput on 8192^3.
+// reads have returned; the first k-step of stage d+1 (certified by the same
+// barrier) is read under the last k-step's 16 MFMAs.  Stage d+2's 16 loads
+// are spread over the 32 MFMAs from that barrier to the end of stage d+1's
+// first k-step, and get at least 32 MFMAs to land.  How tightly the loads
+// are packed decides much of the speed (8192^3, pairs timed on one device):
+// packed into 16 MFMAs, one behind each, is 4% faster than into 8 MFMAs with
+// two behind each, and spreading them over 32 MFMAs gains another 2-2.5%.
 //
 // LDS layout of one stage (64 KiB):  [A: 32 KiB][B: 32 KiB].
 //   K-contiguous operand: 256 rows x 128 bytes of K; chunk c of row r is
@@ -204,13 +205,21 @@ struct WideFrags {
 };
 
 // The whole K loop of one output tile (bf16).  Stage d lives in slot d % 2.
-//   k-steps 0..2: 16 MFMAs each, under which the next k-step is read;
+// Stage d+2's loads go into stage d's slot, which is free from stage d's
+// barrier on, and must have landed by stage d+1's barrier: 32 MFMAs of that
+// window carry them, one load behind every other MFMA (A in stage d's last
+// k-step, B in stage d+1's first).  One load blocks the issuing wave for a
+// few dozen cycles, and the address path serves the four waves in turn, so
+// loads packed closer than that stall the MFMA stream.
+//   k-step 0: 16 MFMAs; k-step 1 read under the first 8; B of stage d+1
+//             loaded behind every other MFMA (into stage d+1's slot);
+//   k-steps 1, 2: 16 MFMAs each, under which the next k-step is read;
 //   sync: wait until none of this wave's loads (only stage d+1's were in
 //         flight) and none of its LDS reads is outstanding; barrier: stage
 //         d+1 is in LDS for every wave, and every wave is done reading stage d;
-//   the side work steps; k-step 3's 16 MFMAs, each followed by one of the 16
-//   loads of stage d+2 (into stage d's slot), with k-step 0 of stage d+1
-//   read under them.
+//   the side work steps; k-step 3: 16 MFMAs; k-step 0 of stage d+1 read
+//             under them; A of stage d+2 loaded behind every other MFMA (into
+//             stage d's slot).
 template <bool AK, bool BK, class SideWork>
 __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, int tm, int tn,
                                               int wave, int lane, SideWork& side) {
@@ -232,12 +241,12 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
   FW f;
   f.init(wm, wn, lane);
   if (KT > 0) {
-    // Prologue: stages 0 and 1 in flight, stage 0 certified, its k-step 0 read.
+    // Prologue: stage 0 and stage 1's A in flight (stage 1's B is loaded in
+    // the first iteration), stage 0 certified, its k-step 0 read.
     la.load_all(0, 0, a.K, wave);
     lb.load_all(0, kB, a.K, wave);
     la.load_all(1, kWideStageBytes, a.K, wave);
-    lb.load_all(1, kWideStageBytes + kB, a.K, wave);
-    wait_vmcnt<16>();
+    wait_vmcnt<8>();
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
@@ -246,8 +255,16 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
     const uint32_t nxt = ((d + 1) & 1) * kWideStageBytes;
     int krem_a, krem_b;
     const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(d + 2, a.K, &krem_a);
-    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(d + 2, a.K, &krem_b);
-    static_for<0, 3>([&](auto kc) {
+    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(d + 1, a.K, &krem_b);
+    static_for<0, 16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      sched_fence();
+      if constexpr (m == 0) f.template read_part<1, 0, 2>(cur, cur + kB);
+      if constexpr (m == 4) f.template read_part<1, 1, 2>(cur, cur + kB);
+      f.template mma<0, m, 1>(acc);
+      if constexpr (m & 1) lb.load(rb, krem_b, nxt + kB, wave, m >> 1);
+    });
+    static_for<1, 3>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
       static_for<0, 2>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
@@ -273,11 +290,7 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
       if constexpr (m == 4) f.template read_part<0, 0, 2>(nxt, nxt + kB);
       if constexpr (m == 8) f.template read_part<0, 1, 2>(nxt, nxt + kB);
       f.template mma<1, m, 1>(acc);
-      if constexpr (m < 8) {
-        la.load(ra, krem_a, cur, wave, m);
-      } else {
-        lb.load(rb, krem_b, cur + kB, wave, m - 8);
-      }
+      if constexpr (m & 1) la.load(ra, krem_a, cur, wave, m >> 1);
       if constexpr (m == 9) side.template compute<0>(lane);
       if constexpr (m == 11) side.template compute<1>(lane);
       if constexpr (m == 13) side.template compute<2>(lane);
