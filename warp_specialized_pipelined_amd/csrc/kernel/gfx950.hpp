@@ -54,11 +54,24 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 //
 // The compiler's hazard pass does not look inside inline assembly, so the
 // wait states the gfx9 family requires before this instruction are part of
-// it: 5 after a VALU write of an SGPR the load reads (the resource comes back
-// from a spill lane with v_readlane when SGPRs run short -- without the wait
-// the load can take a half-updated descriptor), and 1 after the SALU write of
-// M0 that the "{m0}" operand puts right in front of it.  s_nop 4 covers both.
+// it: 1 after the SALU write of M0 that the "{m0}" operand puts right in
+// front of it, and 5 after a VALU write of an SGPR the load reads.  The
+// latter happens when SGPRs run short and the resource comes back from a
+// spill lane with v_readlane right before the load; without the wait the
+// load can take a half-updated descriptor.  dma16 carries 2 wait states,
+// for the K-loop stage loads, whose resources SALU code builds at the top of
+// every iteration; dma16_w5 carries 5, for loads whose resource lives across
+// the K loop (the tile consumer's).  tests/test_asm_hazards.py checks both
+// rules on every LDS-DMA load of every kernel.  Each wait state costs the
+// MFMA stream a cycle: 2 instead of 5 on the 16 stage loads of a stage is
+// worth 2% on 8192^3 bf16.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 1\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+               "{m0}"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void dma16_w5(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
                "{m0}"(m0)

@@ -207,7 +207,7 @@ struct TileConsumer {
 
   __device__ __forceinline__ void fetch(int wave) {
     const int j = fetched++;
-    dma16(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
+    dma16_w5(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
   }
 
   // Read step `folded` back from its landing slot (its fetch must have
