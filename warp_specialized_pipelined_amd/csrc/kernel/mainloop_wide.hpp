@@ -101,10 +101,15 @@ struct WideLoader {
   }
 
   // Load j (0..7) into the stage slot at LDS offset `slot`.  Stages past K
-  // load out of range (zeros into a free slot), like mainloop.hpp's.
+  // load out of range (zeros into a free slot), like mainloop.hpp's.  With
+  // MASK false the stage is known to be complete (krem == kWideK), and the
+  // per-lane K check -- two VALU instructions in front of every load -- is
+  // left out.
+  template <bool MASK = true>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
                                        int j) const {
-    dma16(r, lds_at(slot + (wave * 8 + j) * 1024), (kpos[j] < krem) ? off[j] : kOobOffset);
+    dma16(r, lds_at(slot + (wave * 8 + j) * 1024),
+          (!MASK || kpos[j] < krem) ? off[j] : kOobOffset);
   }
   __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
     int krem;
@@ -250,7 +255,8 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
-  for (int d = 0; d < KT; ++d) {
+  auto iteration = [&](const int d, auto mask_c) {
+    constexpr bool kMask = decltype(mask_c)::value;
     const uint32_t cur = (d & 1) * kWideStageBytes;
     const uint32_t nxt = ((d + 1) & 1) * kWideStageBytes;
     int krem_a, krem_b;
@@ -262,7 +268,7 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
       if constexpr (m == 0) f.template read_part<1, 0, 2>(cur, cur + kB);
       if constexpr (m == 4) f.template read_part<1, 1, 2>(cur, cur + kB);
       f.template mma<0, m, 1>(acc);
-      if constexpr (m & 1) lb.load(rb, krem_b, nxt + kB, wave, m >> 1);
+      if constexpr (m & 1) lb.template load<kMask>(rb, krem_b, nxt + kB, wave, m >> 1);
     });
     static_for<1, 3>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
@@ -290,12 +296,20 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
       if constexpr (m == 4) f.template read_part<0, 0, 2>(nxt, nxt + kB);
       if constexpr (m == 8) f.template read_part<0, 1, 2>(nxt, nxt + kB);
       f.template mma<1, m, 1>(acc);
-      if constexpr (m & 1) la.load(ra, krem_a, cur, wave, m >> 1);
+      if constexpr (m & 1) la.template load<kMask>(ra, krem_a, cur, wave, m >> 1);
       if constexpr (m == 9) side.template compute<0>(lane);
       if constexpr (m == 11) side.template compute<1>(lane);
       if constexpr (m == 13) side.template compute<2>(lane);
     });
-  }
+  };
+  // Iteration d loads B of stage d+1 and A of stage d+2.  While both stages
+  // are complete, the loads need no K check; the last iterations (the K
+  // tail and the stages past K, which only zero a free slot) keep it.
+  int clean = (int)(a.K / kWideK) - 2;
+  clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
+  int d = 0;
+  for (; d < clean; ++d) iteration(d, std::integral_constant<bool, false>{});
+  for (; d < KT; ++d) iteration(d, std::integral_constant<bool, true>{});
   // Every wave is done with the ring, and every load into it has landed,
   // before anyone reuses it.
   sched_fence();
