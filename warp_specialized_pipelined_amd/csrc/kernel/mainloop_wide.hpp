@@ -304,9 +304,15 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
   };
   // Iteration d loads B of stage d+1 and A of stage d+2.  While both stages
   // are complete, the loads need no K check; the last iterations (the K
-  // tail and the stages past K, which only zero a free slot) keep it.
-  int clean = (int)(a.K / kWideK) - 2;
-  clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
+  // tail and the stages past K, which only zero a free slot) keep it.  With
+  // side work the loop stays one copy: the second copy's register pressure
+  // pushed the side work's state to scratch inside the loop, and a scratch
+  // reload waits for every load in flight.
+  int clean = 0;
+  if constexpr (std::is_same<SideWork, NoSideWork>::value) {
+    clean = (int)(a.K / kWideK) - 2;
+    clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
+  }
   int d = 0;
   for (; d < clean; ++d) iteration(d, std::integral_constant<bool, false>{});
   for (; d < KT; ++d) iteration(d, std::integral_constant<bool, true>{});
