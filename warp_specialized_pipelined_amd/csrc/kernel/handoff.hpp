@@ -109,6 +109,13 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
 
+// The value of lane 0 as a wave-uniform one.  The consumer's counters and
+// flags are the same in every lane; saying so keeps them in SGPRs and their
+// branches scalar (the compiler cannot prove it through the hand-off ring's
+// LDS loads and the K loop's phis, and otherwise keeps them in VGPRs with
+// EXEC-masked branches).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // One wave's share of the consumer work on one tile: rows 64w .. 64w+63, two
 // per step.  Step j covers rows 64w + 2j (lanes 0-31) and 64w + 2j + 1 (lanes
 // 32-63); lane l takes the 16 bytes (8 columns) 8 (l % 32) .. + 7 of its row,
@@ -169,7 +176,7 @@ struct TileConsumer {
   __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int wave,
                                         int lane) {
     slot = slot_;
-    const int tile_id = HandoffRing::wait(slot, use);
+    const int tile_id = uni(HandoffRing::wait(slot, use));
     const TileCoord t = tile_of(tile_id, a);
     const int64_t r0 = (int64_t)t.tm * kTileM;
     const int64_t c0 = (int64_t)t.tn * kTileN;
@@ -192,6 +199,12 @@ struct TileConsumer {
     step_bytes = (uint32_t)(2 * a.ldd * 2);
     stat_off = (lane & 31) == 0 ? (uint32_t)(row0 * a.stat_ld * 4) : kOobOffset;
     stat_step = (uint32_t)(2 * a.stat_ld * 4);
+    // Opaque from here on: otherwise the compiler folds `lane_off + j *
+    // step_bytes` back into the 64-bit formula they came from and keeps its
+    // 64-bit parts live across the K loop (spilled, and a scratch reload in
+    // the loop waits for every stage load in flight).
+    asm volatile("" : "+v"(lane_off), "+v"(stat_off));
+    asm volatile("" : "+s"(step_bytes), "+s"(stat_step));
     fetched = 0;
     folded = 0;
     active = true;
@@ -206,7 +219,8 @@ struct TileConsumer {
   }
 
   __device__ __forceinline__ void fetch(int wave) {
-    const int j = fetched++;
+    const int j = uni(fetched);
+    fetched = j + 1;
     dma16_w5(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
   }
 
@@ -214,7 +228,8 @@ struct TileConsumer {
   // completed).
   __device__ __forceinline__ void read_back(int wave, int lane) {
     compiler_fence();
-    fold_j = folded++;
+    fold_j = uni(folded);
+    folded = fold_j + 1;
     v = *(const MIGEMM_LDS u32x4*)lds_at(landing(wave, fold_j) + 16 * lane);
     folding = true;
   }
@@ -225,7 +240,7 @@ struct TileConsumer {
   __device__ __forceinline__ void compute(int lane) {
     // Only 32 of a tile's iterations fold a step; the others skip the work
     // (a uniform branch that jumps over VALU code only, never over MFMAs).
-    if (!folding) return;
+    if (!uni(folding)) return;
     if constexpr (P == 0) {
       const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
       float s = 0.0f;
@@ -274,9 +289,9 @@ struct TileConsumer {
   // Store the pending step's copy and statistics; release the slot after the
   // tile's last step.
   __device__ __forceinline__ void store_pending(int lane) {
-    if (!pending) return;
+    if (!uni(pending)) return;
     pending = false;
-    const int j = pend_j;
+    const int j = uni(pend_j);
     const uint32_t o = at(lane_off, step_bytes, j);
     if (ncols == kTileN) {
       __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, 0);
@@ -302,23 +317,23 @@ struct TileConsumer {
   __device__ __forceinline__ void after_barrier(const KernelArgs& a, int wave, int lane) {
     (void)a;
     store_pending(lane);
-    if (!active) return;
-    if (fetched > folded) read_back(wave, lane);
-    if (fetched < kSteps) fetch(wave);
+    if (!uni(active)) return;
+    if (uni(fetched) > uni(folded)) read_back(wave, lane);
+    if (uni(fetched) < kSteps) fetch(wave);
   }
 
   // After the K loop: finish the tile with up to kConsumerDepth fetches in
   // flight.  newer = fetches issued after the one being waited for.
   __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
-    if (folding) {  // (a K loop always runs its compute parts; kept for safety)
+    if (uni(folding)) {  // (a K loop always runs its compute parts; kept for safety)
       compute<0>(lane);
       compute<1>(lane);
       compute<2>(lane);
     }
     store_pending(lane);
-    while (active) {
-      while (fetched < kSteps && fetched - folded < kConsumerDepth) fetch(wave);
-      const int newer = fetched - folded - 1;
+    while (uni(active)) {
+      while (uni(fetched) < kSteps && uni(fetched) - uni(folded) < kConsumerDepth) fetch(wave);
+      const int newer = uni(fetched) - uni(folded) - 1;
       static_assert(kConsumerDepth <= 4, "drain waits are written for up to 4 fetches in flight");
       if (newer >= 3) {
         wait_vmcnt<3>();

@@ -54,7 +54,14 @@ struct WideLoader {
   int64_t kstep_bytes;             // address step from one stage of K to the next
   int64_t bytes_left;              // operand bytes from tile_base to its end
   uint32_t off[8];                 // this lane's byte offset for load j
-  int32_t kpos[8];                 // K index (within the stage) that load j starts at
+  // The K index (within the stage) that this lane's load j starts at, kept
+  // as the two values it takes (K-contiguous: by the parity of j) or as the
+  // value for j = 0 (MN-contiguous: + 8 j), not as 8 registers.
+  int32_t kq[2];
+  __device__ __forceinline__ int32_t kpos(int j) const {
+    if constexpr (KMAJ) return kq[j & 1];
+    return kq[0] + 8 * j;
+  }
 
   __device__ __forceinline__ void init(const void* ptr, int64_t bytes, int64_t ld, int64_t origin,
                                        int wave, int lane) {
@@ -69,8 +76,10 @@ struct WideLoader {
         const int row = (wave * 8 + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz_k8(row);
         off[j] = (uint32_t)(row * ld * 2) + (uint32_t)(c * 16);
-        kpos[j] = c * 8;
       }
+      // c * 8 for load j: swz_k8 of its row is 4 (j & 1) + (lane >> 4).
+      kq[0] = ((lane & 7) ^ (lane >> 4)) * 8;
+      kq[1] = ((lane & 7) ^ (4 + (lane >> 4))) * 8;
     } else {
       // Load idx = 8 wave + j fills K rows 8 (idx % 8) .. + 7 of panel idx / 8.
       tile_base = p + origin * 2;
@@ -83,8 +92,9 @@ struct WideLoader {
         const int chunk = (lane & 7) ^ swz_mn<2>(krow);
         const int col = (idx / 8) * 64 + chunk * 8;
         off[j] = (uint32_t)(krow * ld * 2) + (uint32_t)(col * 2);
-        kpos[j] = krow;
       }
+      kq[0] = lane >> 3;  // krow of load j is 8 j + (lane >> 3)
+      kq[1] = 0;
     }
   }
 
@@ -109,7 +119,7 @@ struct WideLoader {
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
                                        int j) const {
     dma16(r, lds_at(slot + (wave * 8 + j) * 1024),
-          (!MASK || kpos[j] < krem) ? off[j] : kOobOffset);
+          (!MASK || kpos(j) < krem) ? off[j] : kOobOffset);
   }
   __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
     int krem;
@@ -304,15 +314,11 @@ __device__ __forceinline__ void mainloop_wide(Accum& acc, const KernelArgs& a, i
   };
   // Iteration d loads B of stage d+1 and A of stage d+2.  While both stages
   // are complete, the loads need no K check; the last iterations (the K
-  // tail and the stages past K, which only zero a free slot) keep it.  With
-  // side work the loop stays one copy: the second copy's register pressure
-  // pushed the side work's state to scratch inside the loop, and a scratch
-  // reload waits for every load in flight.
-  int clean = 0;
-  if constexpr (std::is_same<SideWork, NoSideWork>::value) {
-    clean = (int)(a.K / kWideK) - 2;
-    clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
-  }
+  // tail and the stages past K, which only zero a free slot) keep it.  (The
+  // two copies of the body must not push anything to scratch: a scratch
+  // reload inside the loop waits for every stage load in flight.)
+  int clean = (int)(a.K / kWideK) - 2;
+  clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
   int d = 0;
   for (; d < clean; ++d) iteration(d, std::integral_constant<bool, false>{});
   for (; d < KT; ++d) iteration(d, std::integral_constant<bool, true>{});
