@@ -169,7 +169,8 @@ struct TileConsumer {
   }
 
   __device__ __forceinline__ static uint32_t landing(int wave, int c) {
-    return kConsumerSlotOffset + (wave * kConsumerDepth + (c % kConsumerDepth)) * kConsumerSlotBytes;
+    static_assert((kConsumerDepth & (kConsumerDepth - 1)) == 0, "landing slots are indexed with a mask");
+    return kConsumerSlotOffset + (wave * kConsumerDepth + (c & (kConsumerDepth - 1))) * kConsumerSlotBytes;
   }
 
   // Wait for the use-th commit of `slot`, then set up this lane's share.
@@ -181,8 +182,8 @@ struct TileConsumer {
     const int64_t r0 = (int64_t)t.tm * kTileM;
     const int64_t c0 = (int64_t)t.tn * kTileN;
     const int64_t rleft = a.M - r0, cleft = a.N - c0;
-    rows = (int)(rleft < kTileM ? rleft : kTileM);
-    ncols = (int)(cleft < kTileN ? cleft : kTileN);
+    rows = uni((int)(rleft < kTileM ? rleft : kTileM));
+    ncols = uni((int)(cleft < kTileN ? cleft : kTileN));
     row0 = wave * 64 + (lane >> 5);
     const int col = 8 * (lane & 31);
     int64_t bytes = ((a.M - 1 - r0) * a.ldd + (a.N - c0)) * 2;
@@ -214,8 +215,10 @@ struct TileConsumer {
 
   // This lane's offset (from `base`, per step `step`) for step j, or an
   // out-of-range one when the step's row is past the tile's last.
+  // (A select, not a branch: `&` rather than `&&`.)
   __device__ __forceinline__ uint32_t at(uint32_t base, uint32_t step, int j) const {
-    return (base != kOobOffset && row0 + 2 * j < rows) ? base + (uint32_t)j * step : kOobOffset;
+    const bool ok = (base != kOobOffset) & (row0 + 2 * j < rows);
+    return ok ? base + (uint32_t)j * step : kOobOffset;
   }
 
   __device__ __forceinline__ void fetch(int wave) {
@@ -293,7 +296,7 @@ struct TileConsumer {
     pending = false;
     const int j = uni(pend_j);
     const uint32_t o = at(lane_off, step_bytes, j);
-    if (ncols == kTileN) {
+    if (__builtin_expect(ncols == kTileN, 1)) {
       __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, 0);
     } else {
       // A tile cut short by N: column by column, past-N ones out of range.
