@@ -132,9 +132,12 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 //   iteration i+1: after its barrier -- whose wait covered the fetch -- read
 //                  the landing slot back; fold the 16 bytes in between the
 //                  MFMAs that follow (compute<0..2>);
-//   iteration i+2: after its barrier, store the copy and the statistics.
-// Stores leave before the iteration's stage loads, so the stage loads stay
-// the youngest 8 vector memory operations at every wait.  After the K loop
+//   iteration i+2: after its barrier, store the copy.
+// The folds put each row's totals into a lane of two registers (lane L for
+// row 64 w + L), which leave with one store each after the tile's last step:
+// 64 scattered 4-byte entries per instruction instead of 2 per instruction
+// in 64 instructions, which kept the address path busy for hundreds of
+// cycles per step and held up the stage loads behind them.  After the K loop
 // the rest is finished synchronously (drain).
 struct TileConsumer {
   static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
@@ -145,8 +148,7 @@ struct TileConsumer {
   __amdgpu_buffer_rsrc_t src, cpy, rsum, rmax;
   uint32_t lane_off;            // byte offset of this lane's 16 bytes in step 0
   uint32_t step_bytes;          // two rows of D
-  uint32_t stat_off;            // byte offset of this lane's row statistics in step 0
-  uint32_t stat_step;           // two rows of statistics
+  uint32_t stat_lane_off;       // byte offset of the statistics entry of row 64 w + lane
   int row0;                     // this lane's row within the tile in step 0
   int rows;                     // valid rows of the tile
   int ncols;                    // valid columns of the tile
@@ -159,8 +161,12 @@ struct TileConsumer {
   bool folding, pending;
   int fold_j, pend_j;
   u32x4 v;                      // the step's 16 bytes (folding), then its copy (pending)
-  float sum;                    // this lane's chunk sum, then its row's sum
+  float sum;                    // this lane's chunk sum, then its row half's sum
   int32_t mkey;                 // same for the maximum, as an order key
+  // The tile's row statistics, lane L holding row 64 w + L's (filled by the
+  // folds, stored after the last step).
+  float st_sum;
+  int32_t st_max;
 
   __device__ __forceinline__ void idle() {
     active = false;
@@ -198,14 +204,14 @@ struct TileConsumer {
     rmax = make_rsrc(a.row_max + s0, (uint32_t)sbytes);
     lane_off = col < ncols ? (uint32_t)((row0 * a.ldd + col) * 2) : kOobOffset;
     step_bytes = (uint32_t)(2 * a.ldd * 2);
-    stat_off = (lane & 31) == 0 ? (uint32_t)(row0 * a.stat_ld * 4) : kOobOffset;
-    stat_step = (uint32_t)(2 * a.stat_ld * 4);
+    const int srow = wave * 64 + lane;
+    stat_lane_off = srow < rows ? (uint32_t)(srow * a.stat_ld * 4) : kOobOffset;
     // Opaque from here on: otherwise the compiler folds `lane_off + j *
     // step_bytes` back into the 64-bit formula they came from and keeps its
     // 64-bit parts live across the K loop (spilled, and a scratch reload in
     // the loop waits for every stage load in flight).
-    asm volatile("" : "+v"(lane_off), "+v"(stat_off));
-    asm volatile("" : "+s"(step_bytes), "+s"(stat_step));
+    asm volatile("" : "+v"(lane_off), "+v"(stat_lane_off));
+    asm volatile("" : "+s"(step_bytes));
     fetched = 0;
     folded = 0;
     active = true;
@@ -280,17 +286,21 @@ struct TileConsumer {
       const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 48));
       const int32_t m01 = max(__builtin_amdgcn_readlane(mkey, 0), __builtin_amdgcn_readlane(mkey, 16));
       const int32_t m23 = max(__builtin_amdgcn_readlane(mkey, 32), __builtin_amdgcn_readlane(mkey, 48));
-      const bool second = (lane & 32) != 0;
-      sum = second ? s2 + s3 : s0 + s1;
-      mkey = second ? m23 : m01;
+      // Row 2j's totals go to lane 2j of the tile's statistics registers,
+      // row 2j+1's to lane 2j+1; they leave with one store after the last
+      // step.
+      const int r = uni(2 * fold_j);
+      const float sa = s0 + s1, sb = s2 + s3;
+      st_sum = lane == r ? sa : (lane == r + 1 ? sb : st_sum);
+      st_max = lane == r ? m01 : (lane == r + 1 ? m23 : st_max);
       folding = false;
       pending = true;
       pend_j = fold_j;
     }
   }
 
-  // Store the pending step's copy and statistics; release the slot after the
-  // tile's last step.
+  // Store the pending step's copy; after the tile's last step also the row
+  // statistics, and release the slot.
   __device__ __forceinline__ void store_pending(int lane) {
     if (!uni(pending)) return;
     pending = false;
@@ -306,10 +316,11 @@ struct TileConsumer {
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), cpy,
                                               e < n ? o + 2 * e : kOobOffset, 0, 0);
     }
-    const uint32_t so = at(stat_off, stat_step, j);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rsum, so, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_order_key(mkey)), rmax, so, 0, 0);
     if (j == kSteps - 1) {
+      // All 64 rows' statistics at once: 64 lanes, one entry each.
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st_sum), rsum, stat_lane_off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_order_key(st_max)), rmax,
+                                            stat_lane_off, 0, 0);
       active = false;
       // The tile's reads all completed before their values were folded.
       HandoffRing::release(slot, lane);
