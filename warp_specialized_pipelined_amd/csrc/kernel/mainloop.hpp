@@ -148,9 +148,13 @@ struct OperandLoader {
   // the end of K (empty resource) still issues its loads: they fall out of
   // range and write zeros, which keeps the count of loads per iteration
   // fixed; the slot they fill holds no live stage.
+  // With MASK false the stage is known to be complete and the per-lane K
+  // check (two VALU instructions) is left out.
+  template <bool MASK = true>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
                                        int j) const {
-    dma16(r, lds_at(slot + (wave * 4 + j) * 1024), (kpos[j] < krem) ? off[j] : kOobOffset);
+    dma16(r, lds_at(slot + (wave * 4 + j) * 1024),
+          (!MASK || kpos[j] < krem) ? off[j] : kOobOffset);
   }
   __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
     int krem;
@@ -456,10 +460,13 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
-  for (int kt = 0; kt < KT; ++kt) {
-    // Every iteration has the same shape (no branch around MFMAs, so the
-    // accumulators never meet at a join): in the last ones the barrier is
-    // redundant and the half-0 read fetches bytes nobody uses.
+  // Every iteration has the same shape (no branch around MFMAs, so the
+  // accumulators never meet at a join): in the last ones the barrier is
+  // redundant and the half-0 read fetches bytes nobody uses.  Iterations
+  // whose loaded stage (kt+3) lies inside K run a copy of the body without
+  // the loads' per-lane K check.
+  auto iteration = [&](const int kt, auto mask_c) {
+    constexpr bool kMask = decltype(mask_c)::value;
     const uint32_t cur = (kt % kStages) * kStageBytes;
     const uint32_t nxt = ((kt + 1) % kStages) * kStageBytes;
     const uint32_t s3 = ((kt + 3) % kStages) * kStageBytes;
@@ -471,11 +478,11 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     auto loads_after = [&](auto qc) {
       constexpr int q = decltype(qc)::value;
       if constexpr (q < 2) {
-        la.load(ra, krem_a, s3, wave, 2 * q);
-        la.load(ra, krem_a, s3, wave, 2 * q + 1);
+        la.template load<kMask>(ra, krem_a, s3, wave, 2 * q);
+        la.template load<kMask>(ra, krem_a, s3, wave, 2 * q + 1);
       } else {
-        lb.load(rb, krem_b, s3 + kB, wave, 2 * q - 4);
-        lb.load(rb, krem_b, s3 + kB, wave, 2 * q - 3);
+        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, 2 * q - 4);
+        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, 2 * q - 3);
       }
     };
     if constexpr (FH::kBf16) {
@@ -522,26 +529,36 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
       f.template mma<1, 12, 4>(acc);
       side.template compute<2>(lane);
     } else {
-      // A0B1 (B half 0 is free now): the loads, then B half 0 of stage kt+1.
+      // A0B1 (B half 0 is free now), one A load behind each MFMA, then B
+      // half 0 of stage kt+1.
       static_for<0, 4>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         sched_fence();
         f.template mma<2, q, 1>(acc);
-        loads_after(qc);
+        la.template load<kMask>(ra, krem_a, s3, wave, q);
       });
       sched_fence();
       f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
       side.template compute<0>(lane);
-      // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first.
+      // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first,
+      // one B load behind each MFMA.
       sched_fence();
       f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
-      f.template mma<3, 0, 2>(acc);
-      side.template compute<1>(lane);
-      sched_fence();
-      f.template mma<3, 2, 2>(acc);
-      side.template compute<2>(lane);
+      static_for<0, 4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        f.template mma<3, q, 1>(acc);
+        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, q);
+        if constexpr (q == 1) side.template compute<1>(lane);
+        if constexpr (q == 3) side.template compute<2>(lane);
+      });
     }
-  }
+  };
+  int clean = (int)(a.K / kBK) - 3;
+  clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
+  int kt = 0;
+  for (; kt < clean; ++kt) iteration(kt, std::integral_constant<bool, false>{});
+  for (; kt < KT; ++kt) iteration(kt, std::integral_constant<bool, true>{});
   // Every wave is done with the ring, and every load into it (including the
   // zero-filling ones past K) has landed, before anyone reuses it.
   sched_fence();
