@@ -1,5 +1,7 @@
-// mainloop.hpp -- the K loop: an N-stage LDS ring filled by direct
-// global->LDS buffer loads, drained by the MFMA core.
+// mainloop.hpp -- the e4m3 K loop: an N-stage LDS ring filled by direct
+// global->LDS buffer loads, drained by the MFMA core; and the pieces every K
+// loop shares (swizzles, panels, MFMA wrappers, accumulator tile, scheduling
+// helpers).  bf16 runs the 64-deep-stage loop of mainloop_wide.hpp.
 //
 // The CUTLASS pages split this loop between a producer warp that waits for an
 // empty stage, issues the TMA copies for it and lets the transaction barrier
@@ -24,9 +26,9 @@
 // LDS layout of one stage (32 KiB):  [A: 16 KiB][B: 16 KiB].
 //   K-contiguous operand: 256 rows x 64 bytes of K, the four 16-byte chunks
 //     of row r stored in the order c ^ swz_k(r).
-//   MN-contiguous operand: panels of 128 bytes of M or N (64 bf16 or 128
-//     e4m3 columns), each panel holding the stage's (64 / elem_size) K rows
-//     back to back, with the 16-byte chunks of row k permuted by swz_mn(k).
+//   MN-contiguous operand: panels of 128 bytes of M or N (128 e4m3
+//     columns), each panel holding the stage's 64 K rows back to back, with
+//     the 16-byte chunks of row k permuted by swz_mn(k).
 // Both swizzles make the fragment reads of one instruction hit every LDS
 // bank equally often (measured on gfx950: a K-major 16-byte read then takes
 // ~4.5 cycles per instruction instead of 8, and a transposing read ~3.8
@@ -173,27 +175,6 @@ struct OperandLoader {
 template <int ES, bool KMAJ>
 struct FragReader;
 
-// K-contiguous bf16: one ds_read_b128 per fragment.  Rows of a 32-row block
-// start 32 rows apart, so the swizzle depends on the lane alone.
-template <>
-struct FragReader<2, true> {
-  typedef bf16x8 frag_t;
-  static constexpr int kSteps = 2;  // 32 k per stage, 16 per MFMA
-  static constexpr int kReads = 1;  // LDS instructions per fragment
-  uint32_t off[2];                  // per k-step
-  __device__ __forceinline__ void init(int row0, int lane) {
-    const int l = lane & 31;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      off[ks] = (row0 + l) * kStageKBytes + (((2 * ks + (lane >> 5)) ^ swz_k(l)) << 4);
-  }
-  template <int BLK, int KS>
-  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
-    return *reinterpret_cast<const MIGEMM_LDS frag_t*>(
-        lds_at(opnd_base + off[KS] + BLK * 32 * kStageKBytes));
-  }
-};
-
 // K-contiguous e4m3: two ds_read_b128 per fragment (the two 16-byte halves
 // of the lane's 32 bytes of K).
 template <>
@@ -215,45 +196,6 @@ struct FragReader<1, true> {
     const i32x4 hi = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
         lds_at(opnd_base + off[1] + BLK * 32 * kStageKBytes));
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-};
-
-// MN-contiguous bf16: two ds_read_b64_tr_b16 per fragment.  Within each
-// group of 16 lanes the instruction reads a 4 x 16 block of bf16 (lanes
-// 4r..4r+3 each fetch 4 consecutive elements of row r) and hands lane i
-// column i of the block.  Rows are K and columns are M or N here, so each
-// lane receives 4 consecutive k of its own column: lane l gets column l % 32
-// of the block and k = 8 (l / 32) + 0..3 (first read) and + 4..7 (second).
-// A 32-column block is one half of a 64-column panel; the swizzle flips
-// which half depending on k, so even and odd blocks need one lane offset
-// each.
-template <>
-struct FragReader<2, false> {
-  typedef bf16x8 frag_t;
-  static constexpr int kSteps = 2;
-  static constexpr int kReads = 2;
-  uint32_t off[2];  // for even and odd blocks
-  __device__ __forceinline__ void init(int col0, int lane) {
-    const int g = lane >> 4, t = lane & 15;
-    const int k = 8 * (g >> 1) + (t >> 2);
-    const int chunk = 2 * (g & 1) + ((t & 3) >> 1);  // 16-byte chunk within the block's half
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      off[b] = (col0 / 64) * Panel<2>::kBytes + k * kPanelRowBytes +
-               (((4 * b + chunk) ^ swz_mn<2>(k)) << 4) + 8 * (t & 1);
-  }
-  template <int BLK, int KS>
-  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    // k + 16 KS and k + 4 keep swz_mn, so both are constant offsets.
-    constexpr uint32_t c = (BLK >> 1) * Panel<2>::kBytes + 16 * KS * kPanelRowBytes;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c + 4 * kPanelRowBytes));
-    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(frag_t, v);
   }
 };
 
@@ -293,9 +235,21 @@ struct FragReader<1, false> {
   }
 };
 
+// The fragment type of one MFMA operand: 8 bf16 or 32 e4m3 per lane.
 template <int ES>
-__device__ __forceinline__ f32x16 mfma(typename FragReader<ES, true>::frag_t a,
-                                       typename FragReader<ES, true>::frag_t b, f32x16 c);
+struct FragType;
+template <>
+struct FragType<2> {
+  typedef bf16x8 type;
+};
+template <>
+struct FragType<1> {
+  typedef i32x8 type;
+};
+
+template <int ES>
+__device__ __forceinline__ f32x16 mfma(typename FragType<ES>::type a, typename FragType<ES>::type b,
+                                       f32x16 c);
 template <>
 __device__ __forceinline__ f32x16 mfma<2>(bf16x8 a, bf16x8 b, f32x16 c) {
   return mfma_bf16_32x32x16(a, b, c);
@@ -313,21 +267,19 @@ struct Accum {
   f32x16 v[4][4];
 };
 
-// The fragments one wave needs from one stage, in two halves of 32 VGPRs so
-// that one half can be refilled while the MFMAs of the other run.
-//   bf16:  half h = the 4 A and 4 B fragments of k-step h (16 bytes each);
-//          phase 0 = the 16 MFMAs of half 0, phase 1 = those of half 1.
-//   e4m3:  half h = A fragments {2h, 2h+1} and B fragments {2h, 2h+1}
-//          (32 bytes each; the stage is a single k-step); MFMA (i, j) needs
-//          A half i/2 and B half j/2, and the four phases are
-//            phase 0: A0 B0,  phase 1: A1 B0,  phase 2: A0 B1,  phase 3: A1 B1,
-//          so B half 0 is free after phase 1 and A half 0 after phase 2.
+// The e4m3 fragments one wave needs from one stage, in two halves of 32
+// VGPRs so that one half can be refilled while the MFMAs of the other run:
+// half h = A fragments {2h, 2h+1} and B fragments {2h, 2h+1} (32 bytes each;
+// the stage is a single k-step).  MFMA (i, j) needs A half i/2 and B half
+// j/2, and the four phases are
+//   phase 0: A0 B0,  phase 1: A1 B0,  phase 2: A0 B1,  phase 3: A1 B1,
+// so B half 0 is free after phase 1 and A half 0 after phase 2.
 template <int ES, bool AK, bool BK>
 struct FragHalves {
+  static_assert(ES == 1, "bf16 runs mainloop_wide.hpp");
   typedef FragReader<ES, AK> RA;
   typedef FragReader<ES, BK> RB;
-  static constexpr bool kBf16 = RA::kSteps == 2;
-  static constexpr int kPerHalf = kBf16 ? 4 : 2;   // A (and B) fragments per half
+  static constexpr int kPerHalf = 2;   // A (and B) fragments per half
   typename RA::frag_t a[2][kPerHalf];
   typename RB::frag_t b[2][kPerHalf];
   RA ra;
@@ -348,11 +300,9 @@ struct FragHalves {
   __device__ __forceinline__ void read_part(uint32_t a_base, uint32_t b_base) {
     static_for<Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ>([&](auto xc) {
       constexpr int x = decltype(xc)::value;
-      // bf16: block x of k-step H; e4m3: block 2H + x of the single k-step
-      constexpr int blk = kBf16 ? x : 2 * H + x;
-      constexpr int ks = kBf16 ? H : 0;
-      if constexpr ((OPS & 1) != 0) a[H][x] = ra.template read<blk, ks>(a_base);
-      if constexpr ((OPS & 2) != 0) b[H][x] = rb.template read<blk, ks>(b_base);
+      constexpr int blk = 2 * H + x;  // of the stage's single k-step
+      if constexpr ((OPS & 1) != 0) a[H][x] = ra.template read<blk, 0>(a_base);
+      if constexpr ((OPS & 2) != 0) b[H][x] = rb.template read<blk, 0>(b_base);
     });
   }
 
@@ -362,15 +312,9 @@ struct FragHalves {
   __device__ __forceinline__ void mma(Accum& acc) const {
     static_for<FIRST, FIRST + COUNT>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (kBf16) {
-        constexpr int h = P;
-        constexpr int i = m >> 2, j = m & 3;
-        acc.v[i][j] = mfma<ES>(b[h][j], a[h][i], acc.v[i][j]);
-      } else {
-        constexpr int ha = P & 1, hb = P >> 1;  // A and B half of this phase
-        constexpr int i = 2 * ha + (m >> 1), j = 2 * hb + (m & 1);
-        acc.v[i][j] = mfma<ES>(b[hb][m & 1], a[ha][m >> 1], acc.v[i][j]);
-      }
+      constexpr int ha = P & 1, hb = P >> 1;  // A and B half of this phase
+      constexpr int i = 2 * ha + (m >> 1), j = 2 * hb + (m & 1);
+      acc.v[i][j] = mfma<ES>(b[hb][m & 1], a[ha][m >> 1], acc.v[i][j]);
     });
   }
 };
@@ -402,22 +346,20 @@ struct NoSideWork {
   __device__ __forceinline__ void compute(int) {}
 };
 
-// The whole K loop of one output tile.
+// The whole e4m3 K loop of one output tile.
 //
 // Iteration kt works on stage kt, whose half-0 fragments were read during the
 // previous iteration.  The workgroup barrier in the middle certifies stage
 // kt+1 (one ahead):
 //   before:  MFMAs on what is already in registers, under which the rest of
-//            stage kt is read (bf16: half 0's 16 MFMAs with half 1 read in
-//            their first half; e4m3: A0B0 with the half-1 reads, then A1B0);
+//            stage kt is read: A0B0 with the half-1 reads, then A1B0;
 //   sync:    wait until only the previous iteration's 8 loads are in flight
 //            -- those of stage kt+2 -- so this wave's loads of stage kt+1 have
 //            landed; barrier: now stage kt+1 is in LDS for every wave, and
 //            every wave is done reading stage kt-1;
-//   after:   the side work steps once; the MFMAs that remain (bf16: half 1;
-//            e4m3: A0B1, A1B1), the first four each followed by two of the 8
-//            loads of stage kt+3 (into stage kt-1's slot), the next ones
-//            with stage kt+1's half-0 reads.
+//   after:   the side work steps once; A0B1 and A1B1, each MFMA followed by
+//            one of the 8 loads of stage kt+3 (into stage kt-1's slot), with
+//            stage kt+1's half-0 reads between the two phases.
 // Fragment reads are issued early in their phase so that they have landed
 // before anything waits for them (the compiler waits for every LDS read at
 // the top of the loop).  Each stage gets two iterations to land.  Loads of
@@ -429,6 +371,7 @@ template <int ES, bool AK, bool BK, class SideWork>
 __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn, int wave,
                                          int lane, SideWork& side) {
   static_assert(kStages == 4, "the certify-ahead ring is written for 4 stages");
+  static_assert(ES == 1, "bf16 runs mainloop_wide");
   typedef FragHalves<ES, AK, BK> FH;
   constexpr int kBK = kStageKBytes / ES;
   constexpr uint32_t kB = kOperandStageBytes;
@@ -473,86 +416,42 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     int krem_a, krem_b;
     const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(kt + 3, a.K, &krem_a);
     const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(kt + 3, a.K, &krem_b);
-    // The stage-(kt+3) load that follows MFMA q (0..3) of the after-barrier
-    // part: two per MFMA, A first.
-    auto loads_after = [&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      if constexpr (q < 2) {
-        la.template load<kMask>(ra, krem_a, s3, wave, 2 * q);
-        la.template load<kMask>(ra, krem_a, s3, wave, 2 * q + 1);
-      } else {
-        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, 2 * q - 4);
-        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, 2 * q - 3);
-      }
-    };
-    if constexpr (FH::kBf16) {
-      static_for<0, 2>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        f.template read_part<1, q, 2>(cur, cur + kB);
-        f.template mma<0, 4 * q, 4>(acc);
-        interleave_mfma_reads<4, FH::kReadInsts / 2>();
-      });
-      sched_fence();
-      f.template mma<0, 8, 8>(acc);
-    } else {
-      sched_fence();
-      f.template read_part<1, 0, 1, 1>(cur, cur + kB);  // A half 1 first: phase 1 needs it
-      f.template read_part<1, 0, 1, 2>(cur, cur + kB);
-      f.template mma<0, 0, 4>(acc);
-      interleave_mfma_reads<4, FH::kReadInsts>();
-      sched_fence();
-      f.template mma<1, 0, 4>(acc);
-    }
+    sched_fence();
+    f.template read_part<1, 0, 1, 1>(cur, cur + kB);  // A half 1 first: phase 1 needs it
+    f.template read_part<1, 0, 1, 2>(cur, cur + kB);
+    f.template mma<0, 0, 4>(acc);
+    interleave_mfma_reads<4, FH::kReadInsts>();
+    sched_fence();
+    f.template mma<1, 0, 4>(acc);
     sched_fence();
     wait_vmcnt<8>();
     barrier();
     // Anything the side work fetched in the previous iteration left just
     // before that iteration's 8 loads, so the wait above covered it.
     side.after_barrier(a, wave, lane);
-    if constexpr (FH::kBf16) {
-      static_for<0, 4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        f.template mma<1, q, 1>(acc);
-        loads_after(qc);
-      });
-      static_for<0, 2>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        f.template read_part<0, q, 2>(nxt, nxt + kB);
-        f.template mma<1, 4 + 4 * q, 4>(acc);
-        side.template compute<q>(lane);
-        interleave_mfma_reads<4, FH::kReadInsts / 2>();
-      });
+    // A0B1 (B half 0 is free now), one A load behind each MFMA, then B
+    // half 0 of stage kt+1.
+    static_for<0, 4>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
       sched_fence();
-      f.template mma<1, 12, 4>(acc);
-      side.template compute<2>(lane);
-    } else {
-      // A0B1 (B half 0 is free now), one A load behind each MFMA, then B
-      // half 0 of stage kt+1.
-      static_for<0, 4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        f.template mma<2, q, 1>(acc);
-        la.template load<kMask>(ra, krem_a, s3, wave, q);
-      });
+      f.template mma<2, q, 1>(acc);
+      la.template load<kMask>(ra, krem_a, s3, wave, q);
+    });
+    sched_fence();
+    f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
+    side.template compute<0>(lane);
+    // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first,
+    // one B load behind each MFMA.
+    sched_fence();
+    f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
+    static_for<0, 4>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
       sched_fence();
-      f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
-      side.template compute<0>(lane);
-      // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first,
-      // one B load behind each MFMA.
-      sched_fence();
-      f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
-      static_for<0, 4>([&](auto qc) {
-        constexpr int q = decltype(qc)::value;
-        sched_fence();
-        f.template mma<3, q, 1>(acc);
-        lb.template load<kMask>(rb, krem_b, s3 + kB, wave, q);
-        if constexpr (q == 1) side.template compute<1>(lane);
-        if constexpr (q == 3) side.template compute<2>(lane);
-      });
-    }
+      f.template mma<3, q, 1>(acc);
+      lb.template load<kMask>(rb, krem_b, s3 + kB, wave, q);
+      if constexpr (q == 1) side.template compute<1>(lane);
+      if constexpr (q == 3) side.template compute<2>(lane);
+    });
   };
   int clean = (int)(a.K / kBK) - 3;
   clean = clean < 0 ? 0 : (clean > KT ? KT : clean);

@@ -151,8 +151,16 @@ struct WideReader<true> {
   }
 };
 
-// MN-contiguous: two ds_read_b64_tr_b16 (see FragReader<2, false>); k-step
-// ks covers K rows 16 ks .. 16 ks + 15 of the panel.
+// MN-contiguous: two ds_read_b64_tr_b16 per fragment.  Within each group of
+// 16 lanes the instruction reads a 4 x 16 block of bf16 (lanes 4r..4r+3 each
+// fetch 4 consecutive elements of row r) and hands lane i column i of the
+// block.  Rows are K and columns are M or N here, so each lane receives 4
+// consecutive k of its own column: lane l gets column l % 32 of the block and
+// k = 8 (l / 32) + 0..3 (first read) and + 4..7 (second).  A 32-column block
+// is one half of a 64-column panel; the swizzle flips which half depending on
+// k, so even and odd blocks need one lane offset each.  k-step ks covers K
+// rows 16 ks .. 16 ks + 15 of the panel (k + 16 ks and k + 4 keep swz_mn, so
+// both are constant offsets).
 template <>
 struct WideReader<false> {
   static constexpr int kReads = 2;

@@ -13,9 +13,10 @@ constexpr int kTileN = 256;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveTile = 128;
-// Each main-loop stage holds 64 bytes of K for every row of the A and B
-// tiles (32 bf16 or 64 e4m3 values): 16 KiB of A + 16 KiB of B.  Stage s
-// lives in slot s % kStages of the LDS ring.
+// Each stage of the e4m3 K loop holds 64 bytes of K (64 values) for every
+// row of the A and B tiles: 16 KiB of A + 16 KiB of B.  Stage s lives in
+// slot s % kStages of the LDS ring.  (The bf16 loop has its own geometry:
+// 2 slots of 64 KiB, mainloop_wide.hpp.)
 constexpr int kStageKBytes = 64;
 constexpr int kOperandStageBytes = kTileM * kStageKBytes;  // 16 KiB
 constexpr int kStageBytes = 2 * kOperandStageBytes;        // 32 KiB
