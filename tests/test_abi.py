@@ -121,6 +121,23 @@ def test_k_contiguity_rule_only_applies_to_k_contiguous_operands():
     assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_ERR_MISALIGNED
 
 
+@pytest.mark.parametrize("t", [migemm.MIGEMM_BF16, migemm.MIGEMM_FP8_E4M3], ids=["bf16", "e4m3"])
+@pytest.mark.parametrize("operand", ["A", "B"])
+def test_stage_span_of_mn_contiguous_operands(t, operand):
+    # One stage of an MN-contiguous operand is 128 bytes of K (64 bf16 or 128
+    # e4m3 rows of ld elements), so it spans 128 * ld bytes whatever the
+    # type; the loads address it with 32-bit offsets below 2^31.  With
+    # ld = 2^24 a stage is 2^31 bytes: rejected.  (A check that assumed
+    # 64-byte stages would have let it through.)
+    for ld, status in [(2 ** 24, migemm.MIGEMM_ERR_UNSUPPORTED),
+                       (2 ** 24 - 64, migemm.MIGEMM_OK)]:
+        if operand == "A":   # column-major A: M-contiguous, ld between K columns
+            d = migemm.make_desc(256, 256, 256, t, t, 1, ld, 1, 256, 256, 1, 256, 1)
+        else:                # row-major B: N-contiguous, ld between K rows
+            d = migemm.make_desc(256, 256, 256, t, t, 256, 1, ld, 1, 256, 1, 256, 1)
+        assert migemm.gemm_desc_validate(d) == status, (ld, status)
+
+
 def test_empty_and_degenerate_shapes_are_valid():
     for M, N, K in [(0, 0, 0), (0, 16, 16), (16, 0, 16), (16, 16, 0), (1, 1, 8)]:
         d = migemm.make_desc(M, N, K, 1, 1, max(K, 8), 1, max(N, 8), 1, max(N, 8), 1, max(N, 8), 1)

@@ -101,7 +101,8 @@ int validate(const migemm_desc* d, Canon* out) {
          d->c_cs, d->c_rs, d->d_cs, d->d_rs, true};
   }
   // 32-bit buffer offsets: 256 rows of a K-contiguous operand, or one stage
-  // of K rows of an MN-contiguous one, must span less than 2^31 bytes.
+  // of K rows of an MN-contiguous one (128 bytes of K: 64 bf16 or 128 e4m3
+  // rows), must span less than 2^31 bytes.
   const int64_t bk = migemm::kStageKBytes / es;
   Orient ca, cb;
   orient(c.M, c.K, c.a_rs, c.a_cs, &ca);

@@ -9,7 +9,6 @@
 #include "kernel/gfx950.hpp"
 #include "kernel/handoff.hpp"
 #include "kernel/mainloop.hpp"
-#include "kernel/mainloop_wide.hpp"
 #include "kernel/params.hpp"
 #include "kernel/scheduler.hpp"
 #include "launch.h"
@@ -29,18 +28,6 @@ struct LaneIds {
   }
 };
 
-// bf16 runs the 64-deep-stage K loop; e4m3 the 32-deep one (its fragments
-// are twice as wide per k-step and need the split halves of mainloop.hpp).
-template <int ES, bool AK, bool BK, class SideWork>
-__device__ __forceinline__ void k_loop(Accum& acc, const KernelArgs& a, int tm, int tn, int wave,
-                                       int lane, SideWork& side) {
-  if constexpr (ES == 2) {
-    mainloop_wide<AK, BK>(acc, a, tm, tn, wave, lane, side);
-  } else {
-    mainloop<ES, AK, BK>(acc, a, tm, tn, wave, lane, side);
-  }
-}
-
 template <int ES, bool AK, bool BK, bool CONS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
   const int lane = threadIdx.x & 63;
@@ -52,7 +39,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     for (int L = first; L < a.num_tiles; L += gridDim.x) {
       const TileCoord t = tile_of(L, a);
       const LaneIds id(lane, wave);
-      k_loop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none);
+      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none);
       const LaneIds ie(lane, wave);
       epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
       wait_lgkmcnt<0>();  // staging reads done ...
@@ -71,7 +58,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       const TileCoord t = tile_of(L, a);
       if (n > 0) cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
       const LaneIds id(lane, wave);
-      k_loop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, cons);
+      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, cons);
       cons.drain(a, wave, lane);
       const int s = n % kHandoffSlots;
       HandoffRing::acquire(s, n / kHandoffSlots);

@@ -33,7 +33,7 @@ namespace migemm {
 
 // A buffer resource over a row-major bf16 matrix, starting at (r0, c0).
 // round16: extend the range to the end of the last 16-byte block (for reads;
-// range checks work per dword, see OperandLoader::issue).
+// range checks work per dword, see StageLoader::stage_rsrc).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t matrix_rsrc(const void* base, int64_t ld,
                                                               int64_t rows, int64_t cols,
                                                               int64_t r0, int64_t c0, bool round16) {

@@ -193,7 +193,7 @@ struct TileConsumer {
     row0 = wave * 64 + (lane >> 5);
     const int col = 8 * (lane & 31);
     int64_t bytes = ((a.M - 1 - r0) * a.ldd + (a.N - c0)) * 2;
-    bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see OperandLoader::stage_rsrc
+    bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see StageLoader::stage_rsrc
     const uint32_t nb = (uint32_t)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
     src = make_rsrc(static_cast<const unsigned short*>(a.D) + r0 * a.ldd + c0, nb);
     cpy = make_rsrc(static_cast<const unsigned short*>(a.D_copy) + r0 * a.ldd + c0, nb);

@@ -1,7 +1,5 @@
-// mainloop.hpp -- the e4m3 K loop: an N-stage LDS ring filled by direct
-// global->LDS buffer loads, drained by the MFMA core; and the pieces every K
-// loop shares (swizzles, panels, MFMA wrappers, accumulator tile, scheduling
-// helpers).  bf16 runs the 64-deep-stage loop of mainloop_wide.hpp.
+// mainloop.hpp -- the K loop: a 2-slot LDS ring filled by direct
+// global->LDS buffer loads, drained by the MFMA core.
 //
 // The CUTLASS pages split this loop between a producer warp that waits for an
 // empty stage, issues the TMA copies for it and lets the transaction barrier
@@ -13,35 +11,60 @@
 // tile needs 256 of a lane's 512 registers, so every one of the 4 waves is
 // both producer and consumer:
 //   - producer: each wave issues 1/4 of a stage's 16-byte LDS-DMA loads
-//     (buffer_load_dwordx4 ... lds), S-1 stages ahead of the stage being
-//     consumed;
+//     (buffer_load_dwordx4 ... lds), one or two stages ahead of the stage
+//     being consumed;
 //   - full: a wave's own loads have landed when its vmcnt has dropped past
 //     them; all waves' loads have landed after each waited and met at the
 //     workgroup barrier;
 //   - empty: the same barrier also certifies that every wave has finished
-//     reading the stage consumed one step earlier, which is the stage the
-//     new loads overwrite.
+//     reading the stage the new loads overwrite.
 // So the ring needs one s_waitcnt + one s_barrier per stage.
 //
-// LDS layout of one stage (32 KiB):  [A: 16 KiB][B: 16 KiB].
-//   K-contiguous operand: 256 rows x 64 bytes of K, the four 16-byte chunks
-//     of row r stored in the order c ^ swz_k(r).
-//   MN-contiguous operand: panels of 128 bytes of M or N (128 e4m3
-//     columns), each panel holding the stage's 64 K rows back to back, with
-//     the 16-byte chunks of row k permuted by swz_mn(k).
-// Both swizzles make the fragment reads of one instruction hit every LDS
-// bank equally often (measured on gfx950: a K-major 16-byte read then takes
-// ~4.5 cycles per instruction instead of 8, and a transposing read ~3.8
-// instead of 4.5-8).  They are applied on the global side: LDS-DMA writes
-// lane i's 16 bytes to a fixed LDS slot, so each lane fetches the chunk that
-// belongs in its slot.
+// A stage holds 128 bytes of K (64 bf16 or 128 e4m3) per row of each operand
+// tile; the ring has 2 slots of 64 KiB:
+//   - a K-contiguous operand is read in 128-byte row segments (8 lanes per
+//     row), so both 64-byte halves of every line leave in one instruction and
+//     the L1 turns them into one L2 request; with 64-byte segments every
+//     line costs two (measured: L1 misses and L2 requests drop by a third, and
+//     the address path stops stalling on the L1).  MN-contiguous operands are
+//     read in whole 128-byte panel rows.  The memory pipeline serves
+//     requests, not bytes: loads made of 64-byte segments reach only about
+//     half the L2 and HBM throughput of 128-byte ones (~18 vs ~36 TB/s from
+//     L2 over the chip);
+//   - one barrier per 2048 MFMA cycles.
+// With 2 slots, stage d+2 can only be loaded once every wave is done reading
+// stage d.  The last k-step's fragments are read under the k-step before it,
+// so the barrier sits after all but the last k-step's MFMAs, once those reads
+// have returned; the first k-step of stage d+1 (certified by the same
+// barrier) is read under the last k-step's MFMAs.
+//   bf16 (4 k-steps of 16 MFMAs of 32 cycles): the barrier comes after 48 of
+//     the stage's 64 MFMAs; stage d+2's 16 loads are spread over the 32 MFMAs
+//     from that barrier to the end of stage d+1's first k-step (A in stage
+//     d's last k-step, B in stage d+1's first), one behind every other MFMA,
+//     and get at least 32 MFMAs to land.  How tightly the loads are packed
+//     decides much of the speed (8192^3, pairs timed on one device): packed
+//     into 16 MFMAs, one behind each, is 4% faster than into 8 MFMAs with two
+//     behind each, and spreading them over 32 MFMAs gains another 2-2.5%.
+//   e4m3 (2 k-steps of 16 MFMAs of 64 cycles): the barrier comes after the
+//     first k-step; the 16 loads of stage d+2 sit one behind each MFMA of the
+//     second (64 cycles apart, as in bf16), and get at least 16 MFMAs (1024
+//     cycles) to land.  Loads in stage d+1's first k-step would have to land
+//     by the barrier at its end.  (The previous e4m3 loop, 64-byte stages in
+//     a 4-slot ring, was 5.5% slower.)
 //
-// Global side: every LDS-DMA instruction reads whole 128-byte segments (8
-// lanes) for MN-contiguous operands.  The memory pipeline serves requests,
-// not bytes: loads made of 64-byte segments reach only about half the L2 and
-// HBM throughput of 128-byte ones (measured: ~18 vs ~36 TB/s from L2 over
-// the chip).  K-contiguous operands read 64-byte segments (one stage holds
-// 64 bytes of K per row).
+// LDS layout of one stage (64 KiB):  [A: 32 KiB][B: 32 KiB].
+//   K-contiguous operand: 256 rows x 128 bytes of K; chunk c of row r is
+//     stored at chunk c ^ ((r >> 1) & 7).
+//   MN-contiguous operand: panels of 128 bytes of M or N (64 bf16 or 128
+//     e4m3 columns), each holding the stage's K rows (64 or 128) of 128 bytes
+//     back to back; chunk c of K row k stored at c ^ swz_mn(k).
+// The swizzles make the fragment reads of one instruction hit every LDS bank
+// equally often (measured on gfx950: a K-major 16-byte read takes ~4.5 cycles
+// per instruction with a conflict-free pattern instead of 8, a transposing
+// read ~3.8 instead of 4.5-8), and keep every fragment read of a wave at a
+// per-lane base plus an immediate offset.  They are applied on the global
+// side: LDS-DMA writes lane i's 16 bytes to a fixed LDS slot, so each lane
+// fetches the chunk that belongs in its slot.
 #pragma once
 
 #include <type_traits>
@@ -60,11 +83,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// K-contiguous: chunk c of row r is stored at chunk c ^ swz_k(r).  Rows of
-// a fragment block start 32 rows apart, so the value depends on the lane
-// alone.
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
-
 // MN-contiguous: a panel row is 128 bytes of M or N; chunk c of K row k is
 // stored at chunk c ^ swz_mn(k).  bf16 swaps the 64-byte halves of every
 // other pair of rows; e4m3 permutes the four 32-byte pieces.
@@ -73,167 +91,6 @@ __device__ __forceinline__ int swz_mn(int k) {
   return ES == 2 ? ((k >> 1) & 1) << 2 : ((k >> 1) & 3) << 1;
 }
 constexpr int kPanelRowBytes = 128;
-template <int ES>
-struct Panel {
-  static constexpr int kCols = kPanelRowBytes / ES;             // 64 or 128
-  static constexpr int kRows = kStageKBytes / ES;               // K rows: 32 or 64
-  static constexpr int kBytes = kRows * kPanelRowBytes;         // 4 or 8 KiB
-  static constexpr int kLoadsPerPanel = kBytes / 1024;          // 4 or 8
-};
-
-// One operand's share of the ring: where this wave's 4 loads per stage come
-// from and go to.  ES = element size in bytes, KMAJ = K is the contiguous
-// dimension of the operand.
-template <int ES, bool KMAJ>
-struct OperandLoader {
-  static constexpr int kBK = kStageKBytes / ES;     // K per stage, elements
-  static constexpr int kElemsPerChunk = 16 / ES;
-  const unsigned char* tile_base;  // operand address of the tile's (row 0, k 0)
-  int64_t kstep_bytes;             // address step from one stage of K to the next
-  int64_t bytes_left;              // operand bytes from tile_base to its end
-  uint32_t off[4];                 // this lane's byte offset for load j
-  int32_t kpos[4];                 // K index (within the stage) that load j starts at
-
-  // ptr/bytes: the operand; ld: its non-unit stride; origin: first row (M or
-  // N index) of the tile.
-  __device__ __forceinline__ void init(const void* ptr, int64_t bytes, int64_t ld, int64_t origin,
-                                       int wave, int lane) {
-    const unsigned char* p = static_cast<const unsigned char*>(ptr);
-    if constexpr (KMAJ) {
-      tile_base = p + origin * ld * ES;
-      kstep_bytes = kStageKBytes;
-      bytes_left = bytes - origin * ld * ES;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = (wave * 4 + j) * 16 + (lane >> 2);  // 16 rows of 64 B per KiB
-        const int c = (lane & 3) ^ swz_k(row);
-        off[j] = (uint32_t)(row * ld * ES) + (uint32_t)(c * 16);
-        kpos[j] = c * kElemsPerChunk;
-      }
-    } else {
-      // Load idx = 4 * wave + j fills K rows 8 (idx % L) .. + 7 of panel
-      // idx / L (L loads per panel): 8 lanes per 128-byte row.
-      typedef Panel<ES> P;
-      tile_base = p + origin * ES;
-      kstep_bytes = (int64_t)kBK * ld * ES;
-      bytes_left = bytes - origin * ES;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = wave * 4 + j;
-        const int krow = (idx % P::kLoadsPerPanel) * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz_mn<ES>(krow);
-        const int col = (idx / P::kLoadsPerPanel) * P::kCols + chunk * kElemsPerChunk;
-        off[j] = (uint32_t)(krow * ld * ES) + (uint32_t)(col * ES);
-        kpos[j] = krow;
-      }
-    }
-  }
-
-  // A buffer resource over the operand from K stage `kt` on, and the K
-  // elements left in that stage (clamped: only "less than kBK or not"
-  // matters).
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(int kt, int64_t K, int* krem) const {
-    const int64_t step = (int64_t)kt * kstep_bytes;
-    // Buffer range checks work per dword, so an operand whose last row ends
-    // inside a dword would lose its last element: round the range up to 16
-    // bytes.  The base is 16-byte aligned, so the extra bytes share the last
-    // element's 16-byte block (and page) and only feed discarded columns.
-    int64_t left = (bytes_left - step + 15) & ~(int64_t)15;
-    left = left < 0 ? 0 : (left > 0x7FFFFFF0 ? 0x7FFFFFF0 : left);
-    const int64_t krem64 = K - (int64_t)kt * kBK;
-    *krem = krem64 > kBK ? kBK : (int)krem64;
-    return make_rsrc(tile_base + step, (uint32_t)left);
-  }
-
-  // Load j (0..3) of this wave's 4 loads of a stage, from the stage's
-  // resource `r` into the stage slot at LDS offset `slot`.  A stage past
-  // the end of K (empty resource) still issues its loads: they fall out of
-  // range and write zeros, which keeps the count of loads per iteration
-  // fixed; the slot they fill holds no live stage.
-  // With MASK false the stage is known to be complete and the per-lane K
-  // check (two VALU instructions) is left out.
-  template <bool MASK = true>
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
-                                       int j) const {
-    dma16(r, lds_at(slot + (wave * 4 + j) * 1024),
-          (!MASK || kpos[j] < krem) ? off[j] : kOobOffset);
-  }
-  __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
-    int krem;
-    const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt, K, &krem);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) load(r, krem, slot, wave, j);
-  }
-};
-
-// Fragment reads.  A "fragment" is what one lane feeds one 32 x 32 MFMA: 32
-// bytes of K (fp8) or 16 bytes (bf16, one of two k-steps per stage) of one
-// row of A or one column of B.  Each reader keeps the lane's byte offsets of
-// its wave's first 32-row (or -column) block; block BLK and k-step KS sit at
-// a compile-time distance from them, which the LDS instructions take as an
-// immediate offset, so a stage costs one address add per offset.
-template <int ES, bool KMAJ>
-struct FragReader;
-
-// K-contiguous e4m3: two ds_read_b128 per fragment (the two 16-byte halves
-// of the lane's 32 bytes of K).
-template <>
-struct FragReader<1, true> {
-  typedef i32x8 frag_t;
-  static constexpr int kSteps = 1;  // 64 k per stage, 64 per MFMA
-  static constexpr int kReads = 2;
-  uint32_t off[2];                  // per half
-  __device__ __forceinline__ void init(int row0, int lane) {
-    const int l = lane & 31;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      off[h] = (row0 + l) * kStageKBytes + (((2 * (lane >> 5) + h) ^ swz_k(l)) << 4);
-  }
-  template <int BLK, int KS>
-  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
-    const i32x4 lo = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
-        lds_at(opnd_base + off[0] + BLK * 32 * kStageKBytes));
-    const i32x4 hi = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
-        lds_at(opnd_base + off[1] + BLK * 32 * kStageKBytes));
-    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-};
-
-// MN-contiguous e4m3: four ds_read_b64_tr_b8 per fragment.  Within each
-// group of 16 lanes the instruction reads an 8 x 16 block of bytes (lanes 2r
-// and 2r+1 fetch the two halves of row r) and hands lane i column i, i.e. 8
-// consecutive k of its own column: lane l gets column l % 32 of the block and
-// k = 32 (l / 32) + 8 h + 0..7 from read h.  A 32-column block is one 32-byte
-// piece of a 128-column panel, placed by the swizzle, so each of a wave's
-// four blocks has its own lane offset.
-template <>
-struct FragReader<1, false> {
-  typedef i32x8 frag_t;
-  static constexpr int kSteps = 1;
-  static constexpr int kReads = 4;
-  uint32_t off[4];  // per block
-  __device__ __forceinline__ void init(int col0, int lane) {
-    const int g = lane >> 4, t = lane & 15;
-    const int k = 32 * (g >> 1) + (t >> 1);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      off[b] = (col0 / 128) * Panel<1>::kBytes + k * kPanelRowBytes +
-               (((2 * b + (g & 1)) ^ swz_mn<1>(k)) << 4) + 8 * (t & 1);
-  }
-  template <int BLK, int KS>
-  __device__ __forceinline__ frag_t read(uint32_t opnd_base) const {
-    i32x8 v;
-    // k + 8 h keeps swz_mn, so the four reads are constant offsets apart.
-    static_for<0, 4>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (MIGEMM_LDS i32x2*)lds_at(opnd_base + off[BLK] + 8 * h * kPanelRowBytes));
-      v[2 * h] = w[0];
-      v[2 * h + 1] = w[1];
-    });
-    return v;
-  }
-};
 
 // The fragment type of one MFMA operand: 8 bf16 or 32 e4m3 per lane.
 template <int ES>
@@ -267,58 +124,6 @@ struct Accum {
   f32x16 v[4][4];
 };
 
-// The e4m3 fragments one wave needs from one stage, in two halves of 32
-// VGPRs so that one half can be refilled while the MFMAs of the other run:
-// half h = A fragments {2h, 2h+1} and B fragments {2h, 2h+1} (32 bytes each;
-// the stage is a single k-step).  MFMA (i, j) needs A half i/2 and B half
-// j/2, and the four phases are
-//   phase 0: A0 B0,  phase 1: A1 B0,  phase 2: A0 B1,  phase 3: A1 B1,
-// so B half 0 is free after phase 1 and A half 0 after phase 2.
-template <int ES, bool AK, bool BK>
-struct FragHalves {
-  static_assert(ES == 1, "bf16 runs mainloop_wide.hpp");
-  typedef FragReader<ES, AK> RA;
-  typedef FragReader<ES, BK> RB;
-  static constexpr int kPerHalf = 2;   // A (and B) fragments per half
-  typename RA::frag_t a[2][kPerHalf];
-  typename RB::frag_t b[2][kPerHalf];
-  RA ra;
-  RB rb;
-
-  // LDS read instructions of one half.
-  static constexpr int kReadInsts = kPerHalf * (RA::kReads + RB::kReads);
-
-  __device__ __forceinline__ void init(int wm, int wn, int lane) {
-    ra.init(wm * kWaveTile, lane);
-    rb.init(wn * kWaveTile, lane);
-  }
-
-  // Fragments [Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ) of half H from
-  // the stage slots at LDS offsets a_base (A) and b_base (B).
-  // OPS: 1 = A only, 2 = B only, 3 = both.
-  template <int H, int Q, int NQ, int OPS = 3>
-  __device__ __forceinline__ void read_part(uint32_t a_base, uint32_t b_base) {
-    static_for<Q * kPerHalf / NQ, (Q + 1) * kPerHalf / NQ>([&](auto xc) {
-      constexpr int x = decltype(xc)::value;
-      constexpr int blk = 2 * H + x;  // of the stage's single k-step
-      if constexpr ((OPS & 1) != 0) a[H][x] = ra.template read<blk, 0>(a_base);
-      if constexpr ((OPS & 2) != 0) b[H][x] = rb.template read<blk, 0>(b_base);
-    });
-  }
-
-  // MFMAs [FIRST, FIRST + COUNT) of phase P (all indices compile-time, so
-  // every fragment and accumulator stays in registers).
-  template <int P, int FIRST, int COUNT>
-  __device__ __forceinline__ void mma(Accum& acc) const {
-    static_for<FIRST, FIRST + COUNT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      constexpr int ha = P & 1, hb = P >> 1;  // A and B half of this phase
-      constexpr int i = 2 * ha + (m >> 1), j = 2 * hb + (m & 1);
-      acc.v[i][j] = mfma<ES>(b[hb][m & 1], a[ha][m >> 1], acc.v[i][j]);
-    });
-  }
-};
-
 // Scheduling hint for one region: alternate one MFMA with a share of the LDS
 // reads, so that reads are issued under the MFMAs instead of in one burst.
 template <int kMfmas, int kReads>
@@ -346,41 +151,310 @@ struct NoSideWork {
   __device__ __forceinline__ void compute(int) {}
 };
 
-// The whole e4m3 K loop of one output tile.
-//
-// Iteration kt works on stage kt, whose half-0 fragments were read during the
-// previous iteration.  The workgroup barrier in the middle certifies stage
-// kt+1 (one ahead):
-//   before:  MFMAs on what is already in registers, under which the rest of
-//            stage kt is read: A0B0 with the half-1 reads, then A1B0;
-//   sync:    wait until only the previous iteration's 8 loads are in flight
-//            -- those of stage kt+2 -- so this wave's loads of stage kt+1 have
-//            landed; barrier: now stage kt+1 is in LDS for every wave, and
-//            every wave is done reading stage kt-1;
-//   after:   the side work steps once; A0B1 and A1B1, each MFMA followed by
-//            one of the 8 loads of stage kt+3 (into stage kt-1's slot), with
-//            stage kt+1's half-0 reads between the two phases.
-// Fragment reads are issued early in their phase so that they have landed
-// before anything waits for them (the compiler waits for every LDS read at
-// the top of the loop).  Each stage gets two iterations to land.  Loads of
-// stages past K fall out of range and only zero a free slot, so every
-// iteration issues exactly 8 loads per wave.  (Spreading a stage's loads
-// over two iterations was measured to be slower: it costs more in latency
-// budget than it gains in issue smoothness.)
+// Stage geometry for element size ES.
+template <int ES>
+struct StageGeom {
+  static constexpr int kK = kStageKBytes / ES;               // K per stage: 64 bf16, 128 e4m3
+  static constexpr int kKSteps = ES == 2 ? 4 : 2;            // MFMA k-steps per stage (16 / 64 K)
+  static constexpr int kPanelCols = kPanelRowBytes / ES;     // 64 or 128
+  static constexpr int kPanelBytes = kK * kPanelRowBytes;    // 8 or 16 KiB
+  static constexpr int kLoadsPerPanel = kK / 8;              // 8 K rows per load
+  static constexpr int kElemsPerChunk = 16 / ES;
+};
+
+// K-contiguous: chunk c of row r is stored at chunk c ^ swz_k8(r).  Rows of
+// a fragment block start 32 rows apart, so the value depends on the lane
+// alone.
+__device__ __forceinline__ int swz_k8(int row) { return (row >> 1) & 7; }
+
+// One operand's share of a wide stage: this wave's 8 LDS-DMA loads of 1 KiB.
+template <int ES, bool KMAJ>
+struct StageLoader {
+  typedef StageGeom<ES> G;
+  const unsigned char* tile_base;  // operand address of the tile's (row 0, k 0)
+  int64_t kstep_bytes;             // address step from one stage of K to the next
+  int64_t bytes_left;              // operand bytes from tile_base to its end
+  uint32_t off[8];                 // this lane's byte offset for load j
+  // The K index (within the stage) that this lane's load j starts at, kept
+  // as the two values it takes (K-contiguous: by the parity of j) or as the
+  // value for j = 0 (MN-contiguous: + 8 j), not as 8 registers.
+  int32_t kq[2];
+  __device__ __forceinline__ int32_t kpos(int j) const {
+    if constexpr (KMAJ) return kq[j & 1];
+    return kq[0] + 8 * j;
+  }
+
+  __device__ __forceinline__ void init(const void* ptr, int64_t bytes, int64_t ld, int64_t origin,
+                                       int wave, int lane) {
+    const unsigned char* p = static_cast<const unsigned char*>(ptr);
+    if constexpr (KMAJ) {
+      // Load idx = 8 wave + j covers rows 8 idx .. 8 idx + 7, 8 lanes a row.
+      tile_base = p + origin * ld * ES;
+      kstep_bytes = kStageKBytes;
+      bytes_left = bytes - origin * ld * ES;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = (wave * 8 + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz_k8(row);
+        off[j] = (uint32_t)(row * ld * ES) + (uint32_t)(c * 16);
+      }
+      // chunk * elements per chunk for load j: swz_k8 of its row is
+      // 4 (j & 1) + (lane >> 4).
+      kq[0] = ((lane & 7) ^ (lane >> 4)) * G::kElemsPerChunk;
+      kq[1] = ((lane & 7) ^ (4 + (lane >> 4))) * G::kElemsPerChunk;
+    } else {
+      // Load idx = 8 wave + j fills K rows 8 (idx % L) .. + 7 of panel idx / L
+      // (L loads per panel).
+      tile_base = p + origin * ES;
+      kstep_bytes = (int64_t)G::kK * ld * ES;
+      bytes_left = bytes - origin * ES;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int idx = wave * 8 + j;
+        const int krow = (idx % G::kLoadsPerPanel) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_mn<ES>(krow);
+        const int col = (idx / G::kLoadsPerPanel) * G::kPanelCols + chunk * G::kElemsPerChunk;
+        off[j] = (uint32_t)(krow * ld * ES) + (uint32_t)(col * ES);
+      }
+      // krow of load j is 8 j + (lane >> 3), plus 64 for odd waves when a
+      // panel takes 16 loads (e4m3).
+      kq[0] = (G::kLoadsPerPanel == 16 ? 64 * (wave & 1) : 0) + (lane >> 3);
+      kq[1] = 0;
+    }
+  }
+
+  // Resource over the operand from K stage `kt` on, and the stage's valid K
+  // (clamped: only "less than a stage or not" matters).  Buffer range checks
+  // work per dword, so an operand whose last row ends inside a dword would
+  // lose its last element: the range is rounded up to 16 bytes.  The base is
+  // 16-byte aligned, so the extra bytes share the last element's 16-byte
+  // block (and page) and only feed discarded columns.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(int kt, int64_t K, int* krem) const {
+    const int64_t step = (int64_t)kt * kstep_bytes;
+    int64_t left = (bytes_left - step + 15) & ~(int64_t)15;
+    left = left < 0 ? 0 : (left > 0x7FFFFFF0 ? 0x7FFFFFF0 : left);
+    const int64_t krem64 = K - (int64_t)kt * G::kK;
+    *krem = krem64 > G::kK ? G::kK : (int)krem64;
+    return make_rsrc(tile_base + step, (uint32_t)left);
+  }
+
+  // Load j (0..7) into the stage slot at LDS offset `slot`.  Stages past K
+  // load out of range and only zero a free slot, which keeps every
+  // iteration's count of loads fixed.  With
+  // MASK false the stage is known to be complete (krem == kK), and the
+  // per-lane K check -- two VALU instructions in front of every load -- is
+  // left out.
+  template <bool MASK = true>
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
+                                       int j) const {
+    dma16(r, lds_at(slot + (wave * 8 + j) * 1024),
+          (!MASK || kpos(j) < krem) ? off[j] : kOobOffset);
+  }
+  __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
+    int krem;
+    const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt, K, &krem);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load(r, krem, slot, wave, j);
+  }
+};
+
+// Fragment reads from a wide stage: read<BLK, KS> returns the fragment of the
+// wave's 32-row (or -column) block BLK for k-step KS.
+template <int ES, bool KMAJ>
+struct FragReader;
+
+// K-contiguous bf16: one ds_read_b128; k-step ks is chunk 2 ks + (lane / 32).
+template <>
+struct FragReader<2, true> {
+  static constexpr int kReads = 1;
+  uint32_t off[4];  // per k-step
+  __device__ __forceinline__ void init(int row0, int lane) {
+    const int l = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      off[ks] = (row0 + l) * kStageKBytes + (((2 * ks + (lane >> 5)) ^ swz_k8(l)) << 4);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ bf16x8 read(uint32_t opnd_base) const {
+    return *reinterpret_cast<const MIGEMM_LDS bf16x8*>(
+        lds_at(opnd_base + off[KS] + BLK * 32 * kStageKBytes));
+  }
+};
+
+// K-contiguous e4m3: two ds_read_b128 per fragment, the two 16-byte halves
+// of the lane's 32 bytes of K: k-step ks, half h is chunk 4 ks + 2 (lane /
+// 32) + h.
+template <>
+struct FragReader<1, true> {
+  static constexpr int kReads = 2;
+  uint32_t off[2][2];  // per k-step and half
+  __device__ __forceinline__ void init(int row0, int lane) {
+    const int l = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        off[ks][h] =
+            (row0 + l) * kStageKBytes + (((4 * ks + 2 * (lane >> 5) + h) ^ swz_k8(l)) << 4);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ i32x8 read(uint32_t opnd_base) const {
+    const i32x4 lo = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
+        lds_at(opnd_base + off[KS][0] + BLK * 32 * kStageKBytes));
+    const i32x4 hi = *reinterpret_cast<const MIGEMM_LDS i32x4*>(
+        lds_at(opnd_base + off[KS][1] + BLK * 32 * kStageKBytes));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// MN-contiguous bf16: two ds_read_b64_tr_b16 per fragment.  Within each group
+// of 16 lanes the instruction reads a 4 x 16 block of bf16 (lanes 4r..4r+3
+// each fetch 4 consecutive elements of row r) and hands lane i column i of
+// the block.  Rows are K and columns are M or N here, so each lane receives 4
+// consecutive k of its own column: lane l gets column l % 32 of the block and
+// k = 8 (l / 32) + 0..3 (first read) and + 4..7 (second).  A 32-column block
+// is one half of a 64-column panel; the swizzle flips which half depending on
+// k, so even and odd blocks need one lane offset each.  k-step ks covers K
+// rows 16 ks .. 16 ks + 15 of the panel (k + 16 ks and k + 4 keep swz_mn, so
+// both are constant offsets).
+template <>
+struct FragReader<2, false> {
+  typedef StageGeom<2> G;
+  static constexpr int kReads = 2;
+  uint32_t off[2];  // for even and odd blocks
+  __device__ __forceinline__ void init(int col0, int lane) {
+    const int g = lane >> 4, t = lane & 15;
+    const int k = 8 * (g >> 1) + (t >> 2);
+    const int chunk = 2 * (g & 1) + ((t & 3) >> 1);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      off[b] = (col0 / G::kPanelCols) * G::kPanelBytes + k * kPanelRowBytes +
+               (((4 * b + chunk) ^ swz_mn<2>(k)) << 4) + 8 * (t & 1);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ bf16x8 read(uint32_t opnd_base) const {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    constexpr uint32_t c = (BLK >> 1) * G::kPanelBytes + 16 * KS * kPanelRowBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK & 1] + c + 4 * kPanelRowBytes));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// MN-contiguous e4m3: four ds_read_b64_tr_b8 per fragment.  Within each
+// group of 16 lanes the instruction reads an 8 x 16 block of bytes (lanes 2r
+// and 2r+1 fetch the two halves of row r) and hands lane i column i, i.e. 8
+// consecutive k of its own column: lane l gets column l % 32 of the block and
+// k = 32 (l / 32) + 8 h + 0..7 from read h.  The wave's 128 columns are one
+// panel; a 32-column block is one 32-byte piece of it, placed by the
+// swizzle, so each block has its own lane offset.  k-step ks covers K rows
+// 64 ks .. 64 ks + 63 (k + 64 ks and k + 8 h keep swz_mn, so all reads are
+// constant offsets apart).
+template <>
+struct FragReader<1, false> {
+  typedef StageGeom<1> G;
+  static constexpr int kReads = 4;
+  uint32_t off[4];  // per block
+  __device__ __forceinline__ void init(int col0, int lane) {
+    const int g = lane >> 4, t = lane & 15;
+    const int k = 32 * (g >> 1) + (t >> 1);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      off[b] = (col0 / G::kPanelCols) * G::kPanelBytes + k * kPanelRowBytes +
+               (((2 * b + (g & 1)) ^ swz_mn<1>(k)) << 4) + 8 * (t & 1);
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ i32x8 read(uint32_t opnd_base) const {
+    i32x8 v;
+    static_for<0, 4>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MIGEMM_LDS i32x2*)lds_at(
+          opnd_base + off[BLK] + (64 * KS + 8 * h) * kPanelRowBytes));
+      v[2 * h] = w[0];
+      v[2 * h + 1] = w[1];
+    });
+    return v;
+  }
+};
+
+// The fragments of two k-steps (buffer kb holds k-steps of parity kb): 4 A
+// and 4 B fragments each (64 VGPRs for bf16, 128 for e4m3).
+template <int ES, bool AK, bool BK>
+struct Frags {
+  typedef FragReader<ES, AK> RA;
+  typedef FragReader<ES, BK> RB;
+  typedef typename FragType<ES>::type frag_t;
+  static constexpr int kReadInsts = 4 * (RA::kReads + RB::kReads);  // per k-step
+  frag_t a[2][4];
+  frag_t b[2][4];
+  RA ra;
+  RB rb;
+
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    ra.init(wm * kWaveTile, lane);
+    rb.init(wn * kWaveTile, lane);
+  }
+
+  // Blocks [Q * 4 / NQ, (Q + 1) * 4 / NQ) of k-step KS into buffer KS & 1.
+  template <int KS, int Q, int NQ>
+  __device__ __forceinline__ void read_part(uint32_t a_base, uint32_t b_base) {
+    static_for<Q * 4 / NQ, (Q + 1) * 4 / NQ>([&](auto xc) {
+      constexpr int x = decltype(xc)::value;
+      a[KS & 1][x] = ra.template read<x, KS>(a_base);
+      b[KS & 1][x] = rb.template read<x, KS>(b_base);
+    });
+  }
+
+  // MFMAs [FIRST, FIRST + COUNT) of the 16 of buffer KB: MFMA m is block
+  // (m / 4) of A with block (m % 4) of B.
+  template <int KB, int FIRST, int COUNT>
+  __device__ __forceinline__ void mma(Accum& acc) const {
+    static_for<FIRST, FIRST + COUNT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int i = m >> 2, j = m & 3;
+      acc.v[i][j] = mfma<ES>(b[KB][j], a[KB][i], acc.v[i][j]);
+    });
+  }
+};
+
+// The whole K loop of one output tile.  Stage d lives in slot d % 2.
+// bf16, per stage:
+//   k-step 0: 16 MFMAs; k-step 1 read under the first 8, one A and one B
+//             block at a time; B of stage d+1 loaded behind every other MFMA
+//             (into stage d+1's slot, free since stage d-1's barrier);
+//   k-steps 1, 2: 16 MFMAs each, under which the next k-step is read;
+//   sync: wait until none of this wave's loads (only stage d+1's were in
+//         flight) and none of its LDS reads is outstanding; barrier: stage
+//         d+1 is in LDS for every wave, and every wave is done reading stage d;
+//   the side work steps; k-step 3: 16 MFMAs; k-step 0 of stage d+1 read
+//             under them; A of stage d+2 loaded behind every other MFMA (into
+//             stage d's slot).
+// e4m3, per stage:
+//   k-step 0: 16 MFMAs; k-step 1 read under the first 8;
+//   sync and barrier as above;
+//   the side work steps; k-step 1: 16 MFMAs; k-step 0 of stage d+1 read
+//             under them; the 16 loads of stage d+2 behind them, one each.
+// One load blocks the issuing wave for a few dozen cycles, and the address
+// path serves the four waves in turn, so loads packed closer than about 64
+// cycles stall the MFMA stream.
 template <int ES, bool AK, bool BK, class SideWork>
-__device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn, int wave,
-                                         int lane, SideWork& side) {
-  static_assert(kStages == 4, "the certify-ahead ring is written for 4 stages");
-  static_assert(ES == 1, "bf16 runs mainloop_wide");
-  typedef FragHalves<ES, AK, BK> FH;
-  constexpr int kBK = kStageKBytes / ES;
+__device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn,
+                                              int wave, int lane, SideWork& side) {
+  typedef StageGeom<ES> G;
+  typedef Frags<ES, AK, BK> FW;
+  constexpr bool kBf16 = ES == 2;
+  constexpr int kLast = G::kKSteps - 1;
   constexpr uint32_t kB = kOperandStageBytes;
-  OperandLoader<ES, AK> la;
-  OperandLoader<ES, BK> lb;
+  StageLoader<ES, AK> la;
+  StageLoader<ES, BK> lb;
   la.init(a.A, a.a_bytes, a.lda, (int64_t)tm * kTileM, wave, lane);
   lb.init(a.B, a.b_bytes, a.ldb, (int64_t)tn * kTileN, wave, lane);
   const int wm = wave >> 1, wn = wave & 1;
-  int KT = (int)((a.K + kBK - 1) / kBK);
+  int KT = (int)((a.K + G::kK - 1) / G::kK);
   // Opaque per tile, like the lane ids: tests on KT are then made where they
   // are used, not once before the tile loop and held (or spilled, and
   // reloaded with a vmcnt(0)) across it.
@@ -391,75 +465,88 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[i][j] = f32x16{};
 
-  FH f;
+  FW f;
   f.init(wm, wn, lane);
   if (KT > 0) {
-    // Prologue: stages 0..2 in flight, stage 0 certified, its half 0 read.
-    for (int s = 0; s < kStages - 1; ++s) {
-      la.load_all(s, s * kStageBytes, a.K, wave);
-      lb.load_all(s, s * kStageBytes + kB, a.K, wave);
+    // Prologue: stage 0 and stage 1 in flight (bf16: stage 1's B is loaded in
+    // the first iteration), stage 0 certified, its k-step 0 read.
+    la.load_all(0, 0, a.K, wave);
+    lb.load_all(0, kB, a.K, wave);
+    la.load_all(1, kStageBytes, a.K, wave);
+    if constexpr (kBf16) {
+      wait_vmcnt<8>();
+    } else {
+      lb.load_all(1, kStageBytes + kB, a.K, wave);
+      wait_vmcnt<16>();
     }
-    wait_vmcnt<16>();
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
-  // Every iteration has the same shape (no branch around MFMAs, so the
-  // accumulators never meet at a join): in the last ones the barrier is
-  // redundant and the half-0 read fetches bytes nobody uses.  Iterations
-  // whose loaded stage (kt+3) lies inside K run a copy of the body without
-  // the loads' per-lane K check.
-  auto iteration = [&](const int kt, auto mask_c) {
+  auto iteration = [&](const int d, auto mask_c) {
     constexpr bool kMask = decltype(mask_c)::value;
-    const uint32_t cur = (kt % kStages) * kStageBytes;
-    const uint32_t nxt = ((kt + 1) % kStages) * kStageBytes;
-    const uint32_t s3 = ((kt + 3) % kStages) * kStageBytes;
+    const uint32_t cur = (d & 1) * kStageBytes;
+    const uint32_t nxt = ((d + 1) & 1) * kStageBytes;
     int krem_a, krem_b;
-    const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(kt + 3, a.K, &krem_a);
-    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(kt + 3, a.K, &krem_b);
-    sched_fence();
-    f.template read_part<1, 0, 1, 1>(cur, cur + kB);  // A half 1 first: phase 1 needs it
-    f.template read_part<1, 0, 1, 2>(cur, cur + kB);
-    f.template mma<0, 0, 4>(acc);
-    interleave_mfma_reads<4, FH::kReadInsts>();
-    sched_fence();
-    f.template mma<1, 0, 4>(acc);
-    sched_fence();
-    wait_vmcnt<8>();
-    barrier();
-    // Anything the side work fetched in the previous iteration left just
-    // before that iteration's 8 loads, so the wait above covered it.
-    side.after_barrier(a, wave, lane);
-    // A0B1 (B half 0 is free now), one A load behind each MFMA, then B
-    // half 0 of stage kt+1.
-    static_for<0, 4>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
+    const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(d + 2, a.K, &krem_a);
+    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(kBf16 ? d + 1 : d + 2, a.K, &krem_b);
+    static_for<0, 16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       sched_fence();
-      f.template mma<2, q, 1>(acc);
-      la.template load<kMask>(ra, krem_a, s3, wave, q);
+      // k-step 1 read one A and one B block at a time, behind every other
+      // MFMA (in two bursts of six reads it was 1% slower).
+      if constexpr (m % 2 == 0 && m < 8) f.template read_part<1, m / 2, 4>(cur, cur + kB);
+      f.template mma<0, m, 1>(acc);
+      if constexpr (kBf16 && (m & 1)) lb.template load<kMask>(rb, krem_b, nxt + kB, wave, m >> 1);
+    });
+    static_for<1, kLast>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      static_for<0, 2>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        sched_fence();
+        f.template read_part<ks + 1, q, 2>(cur, cur + kB);
+        f.template mma<ks & 1, 4 * q, 4>(acc);
+        interleave_mfma_reads<4, FW::kReadInsts / 2>();
+      });
+      sched_fence();
+      f.template mma<ks & 1, 8, 8>(acc);
     });
     sched_fence();
-    f.template read_part<0, 0, 1, 2>(nxt, nxt + kB);
-    side.template compute<0>(lane);
-    // A1B1 (A half 0 is free now), with A half 0 of stage kt+1 read first,
-    // one B load behind each MFMA.
-    sched_fence();
-    f.template read_part<0, 0, 1, 1>(nxt, nxt + kB);
-    static_for<0, 4>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
+    // The last k-step's fragments are in registers: this wave is done
+    // reading stage d once its reads have returned.
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();
+    barrier();
+    // Anything the side work fetched after the previous barrier has landed.
+    side.after_barrier(a, wave, lane);
+    static_for<0, 16>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       sched_fence();
-      f.template mma<3, q, 1>(acc);
-      lb.template load<kMask>(rb, krem_b, s3 + kB, wave, q);
-      if constexpr (q == 1) side.template compute<1>(lane);
-      if constexpr (q == 3) side.template compute<2>(lane);
+      if constexpr (m % 2 == 0 && m >= 2 && m < 10)
+        f.template read_part<0, (m - 2) / 2, 4>(nxt, nxt + kB);
+      f.template mma<kLast & 1, m, 1>(acc);
+      if constexpr (kBf16) {
+        if constexpr (m & 1) la.template load<kMask>(ra, krem_a, cur, wave, m >> 1);
+      } else {
+        if constexpr (m < 8) la.template load<kMask>(ra, krem_a, cur, wave, m);
+        else lb.template load<kMask>(rb, krem_b, cur + kB, wave, m - 8);
+      }
+      if constexpr (m == 9) side.template compute<0>(lane);
+      if constexpr (m == 11) side.template compute<1>(lane);
+      if constexpr (m == 13) side.template compute<2>(lane);
     });
   };
-  int clean = (int)(a.K / kBK) - 3;
+  // Iteration d loads stage d+2 (bf16: and B of stage d+1).  While those
+  // stages are complete, the loads need no K check; the last iterations (the
+  // K tail and the stages past K, which only zero a free slot) keep it.
+  // (The two copies of the body must not push anything to scratch: a scratch
+  // reload inside the loop waits for every stage load in flight.)
+  int clean = (int)(a.K / G::kK) - 2;
   clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
-  int kt = 0;
-  for (; kt < clean; ++kt) iteration(kt, std::integral_constant<bool, false>{});
-  for (; kt < KT; ++kt) iteration(kt, std::integral_constant<bool, true>{});
-  // Every wave is done with the ring, and every load into it (including the
-  // zero-filling ones past K) has landed, before anyone reuses it.
+  int d = 0;
+  for (; d < clean; ++d) iteration(d, std::integral_constant<bool, false>{});
+  for (; d < KT; ++d) iteration(d, std::integral_constant<bool, true>{});
+  // Every wave is done with the ring, and every load into it has landed,
+  // before anyone reuses it.
   sched_fence();
   wait_vmcnt<0>();
   wait_lgkmcnt<0>();

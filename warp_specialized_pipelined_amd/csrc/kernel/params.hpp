@@ -13,14 +13,13 @@ constexpr int kTileN = 256;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveTile = 128;
-// Each stage of the e4m3 K loop holds 64 bytes of K (64 values) for every
-// row of the A and B tiles: 16 KiB of A + 16 KiB of B.  Stage s lives in
-// slot s % kStages of the LDS ring.  (The bf16 loop has its own geometry:
-// 2 slots of 64 KiB, mainloop_wide.hpp.)
-constexpr int kStageKBytes = 64;
-constexpr int kOperandStageBytes = kTileM * kStageKBytes;  // 16 KiB
-constexpr int kStageBytes = 2 * kOperandStageBytes;        // 32 KiB
-constexpr int kStages = 4;                                 // LDS ring depth
+// Each stage of the K-loop ring holds 128 bytes of K (64 bf16 or 128 e4m3
+// values) for every row of the A and B tiles: 32 KiB of A + 32 KiB of B.
+// Stage s lives in slot s % kStages of the LDS ring.
+constexpr int kStageKBytes = 128;
+constexpr int kOperandStageBytes = kTileM * kStageKBytes;  // 32 KiB
+constexpr int kStageBytes = 2 * kOperandStageBytes;        // 64 KiB
+constexpr int kStages = 2;                                 // LDS ring depth
 constexpr int kRingBytes = kStages * kStageBytes;          // 128 KiB
 constexpr int kLdsLimit = 160 * 1024;                      // LDS per workgroup on gfx950
 // Epilogue staging: each wave's 128 x 128 bf16 quarter of the tile, rows
