@@ -18,7 +18,7 @@ import pytest
 
 from warp_specialized_pipelined_amd import build as _build
 
-LDS_LOAD = re.compile(r"^\s*buffer_load_dwordx4 v\d+, s\[(\d+):(\d+)\], 0 offen lds")
+LDS_LOAD = re.compile(r"^\s*buffer_load_dwordx4 v\d+, s\[(\d+):(\d+)\], 0 offen(?: nt)? lds")
 NEEDED_SGPR = 5
 NEEDED_M0 = 1
 
@@ -104,3 +104,6 @@ def test_checker_sees_the_hazard():
     ok = ["\tv_readlane_b32 s91, v254, 61", "\ts_mov_b32 m0, s34", "\ts_nop 4",
           "\tbuffer_load_dwordx4 v22, s[88:91], 0 offen lds"]
     assert not check_load(ok, 3)
+    # the non-temporal form is checked the same way
+    nt = [x.replace("offen lds", "offen nt lds") for x in lines]
+    assert LDS_LOAD.match(nt[3]) and check_load(nt, 3)

@@ -108,7 +108,7 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
     if (row < rows_left && cols_left > 0) {
       const uint32_t off = d_lane + (uint32_t)(4 * i * a.ldd * 2);
       if (cols_left >= 8) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kCpolNt);
       } else {
         for (int e = 0; e < cols_left; ++e)
           __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), rd,

@@ -60,8 +60,8 @@ constexpr uint32_t kOobOffset = 0x80000000u;
 // spill lane with v_readlane right before the load; without the wait the
 // load can take a half-updated descriptor.  dma16 carries 2 wait states,
 // for the K-loop stage loads, whose resources SALU code builds at the top of
-// every iteration; dma16_w5 carries 5, for loads whose resource lives across
-// the K loop (the tile consumer's).  tests/test_asm_hazards.py checks both
+// every iteration; dma16_w5_nt carries 5, for loads whose resource lives
+// across the K loop (the tile consumer's).  tests/test_asm_hazards.py checks both
 // rules on every LDS-DMA load of every kernel.  Each wait state costs the
 // MFMA stream a cycle: 2 instead of 5 on the 16 stage loads of a stage is
 // worth 2% on 8192^3 bf16.
@@ -71,12 +71,19 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uin
                "{m0}"(m0)
                : "memory");
 }
-__device__ __forceinline__ void dma16_w5(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
+// 5 wait states (see above) and the non-temporal hint (nt): for data read
+// once, which should not displace the operand lines that other compute
+// units still need from the L2.
+__device__ __forceinline__ void dma16_w5_nt(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voffset), "s"(r),
                "{m0}"(m0)
                : "memory");
 }
+
+// Cache-policy operand of the buffer store builtins: the non-temporal hint
+// (nt) for data this kernel writes and does not read back soon.
+constexpr int kCpolNt = 2;
 
 // s_waitcnt encodings (gfx9 family): vmcnt in [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8].  A field at its maximum means "do not wait".

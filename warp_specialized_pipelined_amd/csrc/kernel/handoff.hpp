@@ -87,13 +87,33 @@ struct HandoffRing {
   }
 };
 
-// IEEE total order on non-NaN floats as signed integers (-0 < +0), and back.
-__device__ __forceinline__ int32_t order_key(float x) {
-  const int32_t b = __float_as_int(x);
-  return b ^ ((b >> 31) & 0x7FFFFFFF);
+// Row maxima are tracked as keys of the bf16 codes: the 16-bit order key
+// (a negative value's magnitude bits flipped, so that signed comparison
+// orders the values with -0 < +0), plus 0x7F with 16-bit wrap-around.  The
+// shift moves the NaN codes, whose keys sit just above +inf and just below
+// -inf, below the key of -inf, so a plain signed maximum skips them; every
+// other key keeps its order.  kNoKey lies below every key (columns past N).
+constexpr int32_t kNoKey = -32768;
+constexpr int32_t kKeyNegInf = -32514;  // key of -inf (code 0xFF80)
+
+__device__ __forceinline__ int32_t max_key(uint32_t code) {
+  const uint32_t k = code ^ ((0u - (code >> 15)) & 0x7FFFu);
+  return (int32_t)(int16_t)(uint16_t)(k + 0x7Fu);
 }
-__device__ __forceinline__ float from_order_key(int32_t k) {
-  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+// The keys of the two bf16 codes in a 32-bit word, one per 16-bit half.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ s16x2 max_keys2(uint32_t w) {
+  const s16x2 x = __builtin_bit_cast(s16x2, w);
+  const s16x2 neg = x >> 15;  // 0 or -1 per half
+  const s16x2 flip = {0x7FFF, 0x7FFF};
+  const s16x2 shift = {0x7F, 0x7F};
+  return (x ^ (neg & flip)) + shift;
+}
+// The value a key stands for; -inf when no value was a number.
+__device__ __forceinline__ float max_key_value(int32_t key) {
+  if (key < kKeyNegInf) return -__builtin_inff();
+  const uint32_t k = (uint32_t)(key - 0x7F) & 0xFFFFu;
+  return __uint_as_float((k ^ ((0u - (k >> 15)) & 0x7FFFu)) << 16);
 }
 
 // Butterfly partner values within groups of 32 lanes (DPP): pairs at
@@ -138,7 +158,10 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // 64 scattered 4-byte entries per instruction instead of 2 per instruction
 // in 64 instructions, which kept the address path busy for hundreds of
 // cycles per step and held up the stage loads behind them.  After the K loop
-// the rest is finished synchronously (drain).
+// the rest is finished synchronously (drain): every remaining step is
+// fetched at once into the wave's epilogue staging area, which is idle until
+// the wave's own epilogue, so the drain waits for memory once instead of
+// once per few steps.
 struct TileConsumer {
   static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
   // Buffer resources from the tile's origin: D (fetch) and D_copy (store)
@@ -162,7 +185,7 @@ struct TileConsumer {
   int fold_j, pend_j;
   u32x4 v;                      // the step's 16 bytes (folding), then its copy (pending)
   float sum;                    // this lane's chunk sum, then its row half's sum
-  int32_t mkey;                 // same for the maximum, as an order key
+  int32_t mkey;                 // same for the maximum, as a key (max_key)
   // The tile's row statistics, lane L holding row 64 w + L's (filled by the
   // folds, stored after the last step).
   float st_sum;
@@ -178,10 +201,21 @@ struct TileConsumer {
     static_assert((kConsumerDepth & (kConsumerDepth - 1)) == 0, "landing slots are indexed with a mask");
     return kConsumerSlotOffset + (wave * kConsumerDepth + (c & (kConsumerDepth - 1))) * kConsumerSlotBytes;
   }
+  // Where the drain lands step j: the wave's own epilogue staging area.
+  __device__ __forceinline__ static uint32_t drain_slot(int wave, int j) {
+    static_assert(kSteps * kConsumerSlotBytes <= kStagingWaveBytes,
+                  "a wave's remaining steps must fit in its staging area");
+    return wave * kStagingWaveBytes + j * kConsumerSlotBytes;
+  }
 
   // Wait for the use-th commit of `slot`, then set up this lane's share.
   __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int wave,
                                         int lane) {
+    // The lane id as a value the compiler cannot see through: the per-lane
+    // offsets below are then computed here, per tile, instead of once at the
+    // kernel's start and kept across the K loops in scratch (each reload a
+    // round trip to memory that waits behind every load in flight).
+    asm volatile("" : "+v"(lane));
     slot = slot_;
     const int tile_id = uni(HandoffRing::wait(slot, use));
     const TileCoord t = tile_of(tile_id, a);
@@ -230,17 +264,20 @@ struct TileConsumer {
   __device__ __forceinline__ void fetch(int wave) {
     const int j = uni(fetched);
     fetched = j + 1;
-    dma16_w5(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
+    dma16_w5_nt(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
   }
 
-  // Read step `folded` back from its landing slot (its fetch must have
+  // Read step `folded` back from LDS at `slot` (its fetch must have
   // completed).
-  __device__ __forceinline__ void read_back(int wave, int lane) {
+  __device__ __forceinline__ void read_back_at(uint32_t slot, int lane) {
     compiler_fence();
     fold_j = uni(folded);
     folded = fold_j + 1;
-    v = *(const MIGEMM_LDS u32x4*)lds_at(landing(wave, fold_j) + 16 * lane);
+    v = *(const MIGEMM_LDS u32x4*)lds_at(slot + 16 * lane);
     folding = true;
+  }
+  __device__ __forceinline__ void read_back(int wave, int lane) {
+    read_back_at(landing(wave, uni(folded)), lane);
   }
 
   // The fold, in three parts: the lane's chunk of 8 columns, the tree over
@@ -251,15 +288,33 @@ struct TileConsumer {
     // (a uniform branch that jumps over VALU code only, never over MFMAs).
     if (!uni(folding)) return;
     if constexpr (P == 0) {
-      const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
-      float s = 0.0f;
-      int32_t mk = order_key(-__builtin_inff());
+      float s;
+      int32_t mk;
+      if (__builtin_expect(ncols == kTileN, 1)) {
+        // A whole row slice: no column checks; the maximum on both halves
+        // of each word at once.
+        s = bf16_lo(v[0]);
+        s = s + bf16_hi(v[0]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
-        const float x = e < n ? __uint_as_float(h << 16) : 0.0f;
-        s = e == 0 ? x : s + x;
-        if (e < n && x == x) mk = max(mk, order_key(x));
+        for (int w = 1; w < 4; ++w) {
+          s = s + bf16_lo(v[w]);
+          s = s + bf16_hi(v[w]);
+        }
+        s16x2 m2 = max_keys2(v[0]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) m2 = __builtin_elementwise_max(m2, max_keys2(v[w]));
+        mk = max((int32_t)m2.x, (int32_t)m2.y);
+      } else {
+        const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
+        s = 0.0f;
+        mk = kNoKey;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
+          const float x = e < n ? __uint_as_float(h << 16) : 0.0f;
+          s = e == 0 ? x : s + x;
+          mk = max(mk, e < n ? max_key(h) : kNoKey);
+        }
       }
       sum = s;
       mkey = mk;
@@ -307,7 +362,7 @@ struct TileConsumer {
     const int j = uni(pend_j);
     const uint32_t o = at(lane_off, step_bytes, j);
     if (__builtin_expect(ncols == kTileN, 1)) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, kCpolNt);
     } else {
       // A tile cut short by N: column by column, past-N ones out of range.
       const int n = ncols - 8 * (lane & 31);
@@ -319,7 +374,7 @@ struct TileConsumer {
     if (j == kSteps - 1) {
       // All 64 rows' statistics at once: 64 lanes, one entry each.
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st_sum), rsum, stat_lane_off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_order_key(st_max)), rmax,
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(st_max)), rmax,
                                             stat_lane_off, 0, 0);
       active = false;
       // The tile's reads all completed before their values were folded.
@@ -336,30 +391,30 @@ struct TileConsumer {
     if (uni(fetched) < kSteps) fetch(wave);
   }
 
-  // After the K loop: finish the tile with up to kConsumerDepth fetches in
-  // flight.  newer = fetches issued after the one being waited for.
+  // After the K loop: the steps the loop did not finish.  The ring and this
+  // wave's staging area are idle until this wave's epilogue (every wave
+  // passed the loop's closing barrier; the staging area is the wave's own),
+  // so all remaining fetches go out at once, into the staging area, and the
+  // drain waits for memory once.  A step fetched by the loop but not yet
+  // read back is still in its landing slot.
   __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
+    (void)a;
+    asm volatile("" : "+v"(lane));  // (as in begin: lane offsets computed here, not spilled)
     if (uni(folding)) {  // (a K loop always runs its compute parts; kept for safety)
       compute<0>(lane);
       compute<1>(lane);
       compute<2>(lane);
     }
     store_pending(lane);
+    if (!uni(active)) return;
+    const int f0 = uni(fetched);
+    for (int j = f0; j < kSteps; ++j)
+      dma16_w5_nt(src, lds_at(drain_slot(wave, j)), at(lane_off, step_bytes, j));
+    fetched = kSteps;
+    wait_vmcnt<0>();
     while (uni(active)) {
-      while (uni(fetched) < kSteps && uni(fetched) - uni(folded) < kConsumerDepth) fetch(wave);
-      const int newer = uni(fetched) - uni(folded) - 1;
-      static_assert(kConsumerDepth <= 4, "drain waits are written for up to 4 fetches in flight");
-      if (newer >= 3) {
-        wait_vmcnt<3>();
-      } else if (newer == 2) {
-        wait_vmcnt<2>();
-      } else if (newer == 1) {
-        wait_vmcnt<1>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      read_back(wave, lane);
-      wait_lgkmcnt<0>();  // the read is done before the slot is refilled
+      const int j = uni(folded);
+      read_back_at(j < f0 ? landing(wave, j) : drain_slot(wave, j), lane);
       compute<0>(lane);
       compute<1>(lane);
       compute<2>(lane);
