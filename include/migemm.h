@@ -150,11 +150,17 @@ int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* 
  * waves that stored it and, while the next tile's main loop runs, consumer
  * work waits for it, reads it back from D, and then releases the slot.  For
  * the tile at tile column t = n / 256 it writes, for each row r of the tile,
- *   row_sum[r * ceil(N/256) + t] = fp32 sum of D[r][256t .. min(N,256t+256)-1]
- *                                  taken sequentially from +0.0f in ascending
- *                                  column order over the bf16 values of D,
- *   row_max[r * ceil(N/256) + t] = IEEE maxNum of the same values from -inf,
- * and copies the tile bit for bit into D_copy (same strides as D).
+ * over the bf16 values x_j = D[r][256t + j], j = 0 .. 255 (columns at or
+ * past N read as +0.0 for the sum and are left out of the maximum):
+ *   row_sum[r * ceil(N/256) + t] = fp32 sum in a fixed order: chunk sums
+ *       c_k = (((x_8k + x_8k+1) + x_8k+2) + ...) + x_8k+7, k = 0 .. 31, then
+ *       a balanced binary tree over c_0 .. c_31, adjacent pairs first
+ *       (c_0 + c_1, c_2 + c_3, ...; then pairs of those; ...),
+ *   row_max[r * ceil(N/256) + t] = the largest x_j that is not a NaN, with
+ *       -0 < +0; -inf if there is none,
+ * and copies the tile bit for bit into D_copy (same strides as D).  (The
+ * pages leave the consumer's arithmetic open; this order lets 32 lanes
+ * share a row.)
  * row_sum and row_max are M x ceil(N/256) fp32, row-major, 4-byte aligned;
  * D_copy is 16-byte aligned and must not overlap D.  Requires a plan created
  * with MIGEMM_F_TILE_CONSUMER and a row-major D. */
