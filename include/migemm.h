@@ -60,6 +60,16 @@ typedef enum migemm_status {
 
 /* Plan flags. */
 #define MIGEMM_F_TILE_CONSUMER 0x1u /* plan may run gemm_run_with_tile_consumer */
+/* Stream-K (the kernel page's stream-K scheduler and fixup): the tiles of the
+ * last round are cut into K ranges shared by every workgroup, so that no
+ * compute unit idles while others finish whole tiles; the partial sums of a
+ * split tile are added through the workspace.  gemm_run only (UNSUPPORTED
+ * with MIGEMM_F_TILE_CONSUMER).  MIGEMM_F_STREAM_K lets the plan choose it
+ * where its cost model predicts a gain (moving the partials costs about as
+ * much as 24 K stages of MFMA work); MIGEMM_F_STREAM_K_FORCE uses it whenever
+ * K > 0.  gemm_plan_get_info reports the choice (stream_k_tiles). */
+#define MIGEMM_F_STREAM_K 0x2u
+#define MIGEMM_F_STREAM_K_FORCE 0x4u
 
 /* Output tile of the persistent scheduler (and the hand-off unit). */
 #define MIGEMM_TILE_M 256
@@ -112,6 +122,9 @@ typedef struct migemm_plan_info {
   int32_t b_kmajor;        /* 1: B (after any swap) is K-contiguous */
   int32_t cu_count;        /* compute units of the device */
   int32_t handoff_slots;   /* depth of the tile hand-off ring */
+  int64_t stream_k_tiles;  /* tiles cut into K ranges (0: every tile is taken whole) */
+  int32_t stream_k_units_per_tile; /* K stages (tile_k each) per such tile */
+  int32_t reserved;
 } migemm_plan_info;
 
 typedef struct migemm_plan migemm_plan; /* opaque, host memory only */
@@ -133,15 +146,34 @@ int gemm_plan_destroy(migemm_plan* plan);
 int gemm_plan_get_info(const migemm_plan* plan, migemm_plan_info* out);
 
 /* Bytes of device workspace gemm_run needs (the pages' get_workspace_size).
- * The static persistent scheduler needs none: 0.  `workspace` arguments
- * below may then be NULL. */
+ * Plans without stream-K tiles need none: 0, and `workspace` arguments below
+ * may then be NULL.  A stream-K plan needs grid x 512 KiB of fp32 partial
+ * tiles (two per workgroup) plus one 32-bit arrival counter per stream-K tile
+ * and wave (rounded up to 256 bytes). */
 size_t gemm_plan_workspace_size(const migemm_plan* plan);
+
+/* Make `workspace` (gemm_plan_workspace_size(plan) bytes of device memory,
+ * 256-byte aligned, owned by the caller) ready for the plan's runs (the
+ * pages' initialize_workspace): zeroes the arrival counters, with a kernel
+ * enqueued on `stream` (so it may be captured in a HIP graph).  Every run
+ * that completes leaves the counters at zero again; call this before the
+ * first run, after a run that did not complete, and before a workspace is
+ * used with another plan.  A no-op returning OK when the size is 0.
+ * Errors: INVALID_ARG (NULL plan, or NULL workspace with a nonzero size),
+ * MISALIGNED, DEVICE (current device is not the plan's), LAUNCH. */
+int gemm_workspace_init(const migemm_plan* plan, void* workspace, void* stream);
 
 /* D = alpha*A*B + beta*C, enqueued on `stream` (a hipStream_t; NULL = the
  * null stream).  A, B, D must be non-NULL and 16-byte aligned; C may be NULL
  * only when beta == 0, in which case C is never read (it may hold NaN).
  * With K == 0, D = beta*C.  M == 0 or N == 0 is a no-op.  C may alias D only
- * with identical strides.  Asynchronous: returns once the kernel is queued. */
+ * with identical strides.  Asynchronous: returns once the kernel is queued.
+ * `workspace`: NULL when gemm_plan_workspace_size(plan) is 0; otherwise that
+ * many bytes, 256-byte aligned, prepared by gemm_workspace_init (else
+ * INVALID_ARG / MISALIGNED).  Runs that share a workspace must not overlap
+ * in time.  With stream-K the fp32 partial sums of a tile are added in the
+ * order of their K ranges, so a plan gives the same D on every run; plans
+ * with another grid size can round differently in the last bit. */
 int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* C, void* D,
              float alpha, float beta, void* workspace, void* stream);
 

@@ -106,6 +106,12 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(flags=migemm.MIGEMM_F_TILE_CONSUMER, c_rs=1, c_cs=4000, d_rs=1, d_cs=4000),
      migemm.MIGEMM_ERR_UNSUPPORTED),                                        # consumer needs row D
     (dict(flags=0x80), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=migemm.MIGEMM_F_STREAM_K_FORCE), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_STREAM_K_FORCE | migemm.MIGEMM_F_TILE_CONSUMER),
+     migemm.MIGEMM_ERR_UNSUPPORTED),
+    (dict(flags=migemm.MIGEMM_F_STREAM_K), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_TILE_CONSUMER),
+     migemm.MIGEMM_ERR_UNSUPPORTED),                                        # consumer: whole tiles
     (dict(max_workgroups=-1), migemm.MIGEMM_ERR_INVALID_ARG),
     (dict(K=5001, a_rs=5008), migemm.MIGEMM_ERR_MISALIGNED),                # K-contiguous A, K%8
 ])
@@ -163,6 +169,7 @@ def test_null_arguments_are_rejected_without_a_device():
     assert lib.gemm_plan_get_info(None, None) == migemm.MIGEMM_ERR_INVALID_ARG
     assert lib.gemm_plan_destroy(None) == migemm.MIGEMM_OK
     assert migemm.gemm_plan_workspace_size(None) == 0
+    assert lib.gemm_workspace_init(None, None, None) == migemm.MIGEMM_ERR_INVALID_ARG
 
 
 @pytest.mark.skipif(have_gpu(), reason="checks the no-device path")

@@ -24,6 +24,10 @@ struct migemm_plan {
   int grid;
   int cu_count;
   int device;
+  // Stream-K workspace: arrival counters, then the partial tiles.
+  int64_t sk_counters;        // 32-bit counters
+  size_t sk_counter_bytes;    // rounded up to 256 bytes
+  size_t workspace_bytes;
 };
 
 namespace {
@@ -71,7 +75,10 @@ int validate(const migemm_desc* d, Canon* out) {
   if (!d) return MIGEMM_ERR_INVALID_ARG;
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0)
     return MIGEMM_ERR_INVALID_ARG;
-  if ((d->flags & ~MIGEMM_F_TILE_CONSUMER) != 0) return MIGEMM_ERR_INVALID_ARG;
+  constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
+  if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | kStreamK)) != 0) return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & MIGEMM_F_TILE_CONSUMER) && (d->flags & kStreamK))
+    return MIGEMM_ERR_UNSUPPORTED;  // the consumer works on whole tiles
   const int es = elem_size(d->a_type);
   if (es == 0 || elem_size(d->b_type) == 0 || elem_size(d->c_type) == 0 ||
       elem_size(d->d_type) == 0)
@@ -119,6 +126,23 @@ int validate(const migemm_desc* d, Canon* out) {
     return MIGEMM_ERR_UNSUPPORTED;
   if (out) *out = c;
   return MIGEMM_OK;
+}
+
+// Stream-K pays when the stages one workgroup runs, plus the fixup, come
+// below those of whole tiles.  Whole tiles take ceil(T / G) rounds of KT
+// stages; stream-K takes sk_first / G whole rounds, then ceil(units / G)
+// stages, plus the fixup: two 256 KiB fp32 partials written and one read per
+// split tile, which costs about as much as 24 stages on MI355X (fitted to
+// 4000x3000x5000, 8192x1024x8192 and 2048x2048x8192 bf16).  When the units
+// fall on tile boundaries nothing is split and whole tiles are the same.
+constexpr int64_t kSkFixupStages = 24;
+
+bool stream_k_pays(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
+  const int64_t units = (T - sk_first) * kt;
+  if (units % G == 0 && (units / G) % kt == 0) return false;
+  const int64_t whole = (T + G - 1) / G * kt;
+  const int64_t split = sk_first / G * kt + (units + G - 1) / G + kSkFixupStages;
+  return split < whole;
 }
 
 bool trace_enabled() {
@@ -185,7 +209,28 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
 
   int grid = p->cu_count;
   if (desc->max_workgroups > 0 && desc->max_workgroups < grid) grid = desc->max_workgroups;
-  if (a.num_tiles < grid) grid = a.num_tiles;
+  const int64_t kt = (c.K + migemm::kStageKBytes / es - 1) / (migemm::kStageKBytes / es);
+  a.sk_kt = (int32_t)kt;
+  a.sk_first = a.num_tiles;
+  // Whole tiles for all but the last round (when there are at least two),
+  // then the remaining tiles as K-stage units over the whole grid.
+  const int T = a.num_tiles;
+  const int sk_first = T >= 2 * grid ? (T / grid - 1) * grid : 0;
+  const bool sk = kt > 0 && T > 0 &&
+                  ((desc->flags & MIGEMM_F_STREAM_K_FORCE) ||
+                   ((desc->flags & MIGEMM_F_STREAM_K) && stream_k_pays(T, grid, kt, sk_first)));
+  if (sk) {
+    a.sk_first = sk_first;
+    const int64_t units = (int64_t)(T - a.sk_first) * kt;
+    if (units < grid) grid = (int)units;  // every workgroup gets a unit
+    p->sel.stream_k = true;
+    p->sk_counters = (int64_t)(T - a.sk_first) * migemm::kWaves;
+    p->sk_counter_bytes = (size_t)((p->sk_counters * 4 + 255) / 256 * 256);
+    p->workspace_bytes = p->sk_counter_bytes + (size_t)grid * migemm::kSkPartialSlots *
+                                                   (size_t)migemm::kSkPartialBytes;
+  } else if (a.num_tiles < grid) {
+    grid = a.num_tiles;
+  }
   p->grid = grid;
 
   hipError_t e = migemm::prepare_kernel(p->sel);
@@ -201,11 +246,12 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   if (trace_enabled()) {
     std::fprintf(stderr,
                  "[migemm] plan M=%lld N=%lld K=%lld es=%d A:%s B:%s swapped=%d tiles=%dx%d "
-                 "grid=%d group_m=%d lds=%d stages=%d cus=%d\n",
+                 "grid=%d group_m=%d lds=%d stages=%d cus=%d stream_k_tiles=%d workspace=%zu\n",
                  (long long)c.M, (long long)c.N, (long long)c.K, es,
                  p->sel.a_kmajor ? "K-contig" : "M-contig", p->sel.b_kmajor ? "K-contig" : "N-contig",
                  (int)c.swapped, a.tiles_m, a.tiles_n, grid, a.group_m,
-                 migemm::kernel_lds_bytes(p->sel), migemm::kStages, p->cu_count);
+                 migemm::kernel_lds_bytes(p->sel), migemm::kStages, p->cu_count,
+                 p->sel.stream_k ? a.num_tiles - a.sk_first : 0, p->workspace_bytes);
   }
   *out = p;
   return MIGEMM_OK;
@@ -234,17 +280,30 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
   out->b_kmajor = p->sel.b_kmajor ? 1 : 0;
   out->cu_count = p->cu_count;
   out->handoff_slots = migemm::kHandoffSlots;
+  out->stream_k_tiles = p->sel.stream_k ? p->base.num_tiles - p->base.sk_first : 0;
+  out->stream_k_units_per_tile = p->sel.stream_k ? p->base.sk_kt : 0;
   return MIGEMM_OK;
 }
 
 size_t gemm_plan_workspace_size(const migemm_plan* plan) {
-  (void)plan;
-  return 0;
+  return plan ? plan->workspace_bytes : 0;
+}
+
+int gemm_workspace_init(const migemm_plan* p, void* workspace, void* stream) {
+  if (!p) return MIGEMM_ERR_INVALID_ARG;
+  if (p->workspace_bytes == 0) return MIGEMM_OK;
+  if (!workspace) return MIGEMM_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return MIGEMM_ERR_DEVICE;
+  hipError_t e = migemm::launch_zero_words(static_cast<uint32_t*>(workspace), p->sk_counters,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIGEMM_OK : MIGEMM_ERR_LAUNCH;
 }
 
 static int run_common(const migemm_plan* p, const void* A, const void* B, const void* C, void* D,
                       float alpha, float beta, bool consumer, float* row_sum, float* row_max,
-                      void* D_copy, void* stream) {
+                      void* D_copy, void* workspace, void* stream) {
   if (!p) return MIGEMM_ERR_INVALID_ARG;
   if (consumer && !(p->desc.flags & MIGEMM_F_TILE_CONSUMER)) return MIGEMM_ERR_INVALID_ARG;
   if (p->M == 0 || p->N == 0) return MIGEMM_OK;
@@ -258,6 +317,10 @@ static int run_common(const migemm_plan* p, const void* A, const void* B, const 
         !aligned16(D_copy))
       return MIGEMM_ERR_MISALIGNED;
     if (!(p->base.tiles_n > 0)) return MIGEMM_ERR_INVALID_ARG;
+  }
+  if (p->workspace_bytes > 0) {
+    if (!workspace) return MIGEMM_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
   }
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return MIGEMM_ERR_DEVICE;
@@ -273,6 +336,10 @@ static int run_common(const migemm_plan* p, const void* A, const void* B, const 
   a.D_copy = D_copy;
   a.alpha = alpha;
   a.beta = beta;
+  if (p->sel.stream_k) {
+    a.sk_arrivals = static_cast<uint32_t*>(workspace);
+    a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->sk_counter_bytes);
+  }
   KernelSelect s = p->sel;
   s.consumer = consumer;
   hipError_t e = migemm::launch_gemm(s, a, p->grid, static_cast<hipStream_t>(stream));
@@ -281,15 +348,15 @@ static int run_common(const migemm_plan* p, const void* A, const void* B, const 
 
 int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* C, void* D,
              float alpha, float beta, void* workspace, void* stream) {
-  (void)workspace;
-  return run_common(plan, A, B, C, D, alpha, beta, false, nullptr, nullptr, nullptr, stream);
+  return run_common(plan, A, B, C, D, alpha, beta, false, nullptr, nullptr, nullptr, workspace,
+                    stream);
 }
 
 int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const void* B,
                                 const void* C, void* D, float alpha, float beta, float* row_sum,
                                 float* row_max, void* D_copy, void* workspace, void* stream) {
-  (void)workspace;
-  return run_common(plan, A, B, C, D, alpha, beta, true, row_sum, row_max, D_copy, stream);
+  return run_common(plan, A, B, C, D, alpha, beta, true, row_sum, row_max, D_copy, workspace,
+                    stream);
 }
 
 const char* gemm_status_string(int status) {

@@ -2,7 +2,9 @@
 //
 // One workgroup of 4 waves per compute unit.  For every tile the scheduler
 // hands it, the workgroup runs the pipelined K loop into a 256 x 256 fp32
-// accumulator tile (128 x 128 per wave) and then the epilogue.
+// accumulator tile (128 x 128 per wave) and then the epilogue.  Stream-K
+// kernels then take their range of K-stage units of the remaining tiles
+// (streamk.hpp).
 #include <hip/hip_runtime.h>
 
 #include "kernel/epilogue.hpp"
@@ -11,6 +13,7 @@
 #include "kernel/mainloop.hpp"
 #include "kernel/params.hpp"
 #include "kernel/scheduler.hpp"
+#include "kernel/streamk.hpp"
 #include "launch.h"
 
 namespace migemm {
@@ -28,15 +31,17 @@ struct LaneIds {
   }
 };
 
-template <int ES, bool AK, bool BK, bool CONS>
+template <int ES, bool AK, bool BK, bool CONS, bool SK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
+  static_assert(!(CONS && SK), "the tile consumer runs on whole tiles only");
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int first = persistent_slot(blockIdx.x, gridDim.x);
   Accum acc;
   if constexpr (!CONS) {
     NoSideWork none;
-    for (int L = first; L < a.num_tiles; L += gridDim.x) {
+    const int whole = SK ? a.sk_first : a.num_tiles;  // tiles taken whole
+    for (int L = first; L < whole; L += gridDim.x) {
       const TileCoord t = tile_of(L, a);
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none);
@@ -45,6 +50,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       wait_lgkmcnt<0>();  // staging reads done ...
       barrier();          // ... in every wave before the ring is refilled
     }
+    if constexpr (SK) stream_k_tiles<ES, AK, BK>(acc, a, first, gridDim.x, lane, wave);
   } else {
     // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
     // The consumer stage of tile n runs inside tile n+1's K loop; the last
@@ -77,19 +83,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
 
 typedef void (*kernel_fn)(KernelArgs);
 
+template <int ES, bool CONS, bool SK>
+static kernel_fn pick(bool ak, bool bk) {
+  if (ak) return bk ? gemm_kernel<ES, true, true, CONS, SK> : gemm_kernel<ES, true, false, CONS, SK>;
+  return bk ? gemm_kernel<ES, false, true, CONS, SK> : gemm_kernel<ES, false, false, CONS, SK>;
+}
+
 template <int ES>
-static kernel_fn pick(bool ak, bool bk, bool cons) {
-  if (cons) {
-    if (ak) return bk ? gemm_kernel<ES, true, true, true> : gemm_kernel<ES, true, false, true>;
-    return bk ? gemm_kernel<ES, false, true, true> : gemm_kernel<ES, false, false, true>;
-  }
-  if (ak) return bk ? gemm_kernel<ES, true, true, false> : gemm_kernel<ES, true, false, false>;
-  return bk ? gemm_kernel<ES, false, true, false> : gemm_kernel<ES, false, false, false>;
+static kernel_fn pick_mode(const KernelSelect& s) {
+  if (s.consumer) return pick<ES, true, false>(s.a_kmajor, s.b_kmajor);
+  if (s.stream_k) return pick<ES, false, true>(s.a_kmajor, s.b_kmajor);
+  return pick<ES, false, false>(s.a_kmajor, s.b_kmajor);
 }
 
 static kernel_fn select(const KernelSelect& s) {
-  return s.elem_bytes == 2 ? pick<2>(s.a_kmajor, s.b_kmajor, s.consumer)
-                           : pick<1>(s.a_kmajor, s.b_kmajor, s.consumer);
+  return s.elem_bytes == 2 ? pick_mode<2>(s) : pick_mode<1>(s);
 }
 
 int kernel_lds_bytes(const KernelSelect& sel) {
@@ -104,6 +112,22 @@ hipError_t prepare_kernel(const KernelSelect& sel) {
 
 hipError_t launch_gemm(const KernelSelect& sel, const KernelArgs& args, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(select(sel), dim3(grid), dim3(kThreads), kernel_lds_bytes(sel), stream, args);
+  return hipGetLastError();
+}
+
+// Zero the stream-K arrival counters (a fill kernel rather than a memset,
+// so that the call may be captured in a HIP graph).
+__global__ void zero_words(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  blocks = blocks > 1024 ? 1024 : blocks;
+  hipLaunchKernelGGL(zero_words, dim3(blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

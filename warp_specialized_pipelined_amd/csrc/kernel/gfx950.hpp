@@ -81,9 +81,13 @@ __device__ __forceinline__ void dma16_w5_nt(__amdgpu_buffer_rsrc_t r, lds_u8* ld
                : "memory");
 }
 
-// Cache-policy operand of the buffer store builtins: the non-temporal hint
-// (nt) for data this kernel writes and does not read back soon.
+// Cache-policy operand of the buffer load/store builtins: the non-temporal
+// hint (nt) for data this kernel writes and does not read back soon; device
+// scope (sc1) for data other XCDs read during the kernel -- the encoding of
+// an agent-scope relaxed atomic load or store, which misses any stale copy
+// in the XCD's private L2 and writes through it.
 constexpr int kCpolNt = 2;
+constexpr int kCpolDevice = 16;
 
 // s_waitcnt encodings (gfx9 family): vmcnt in [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8].  A field at its maximum means "do not wait".

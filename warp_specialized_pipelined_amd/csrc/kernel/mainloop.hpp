@@ -421,7 +421,7 @@ struct Frags {
   }
 };
 
-// The whole K loop of one output tile.  Stage d lives in slot d % 2.
+// The K loop of one output tile.  Stage d lives in slot d % 2.
 // bf16, per stage:
 //   k-step 0: 16 MFMAs; k-step 1 read under the first 8, one A and one B
 //             block at a time; B of stage d+1 loaded behind every other MFMA
@@ -441,9 +441,15 @@ struct Frags {
 // One load blocks the issuing wave for a few dozen cycles, and the address
 // path serves the four waves in turn, so loads packed closer than about 64
 // cycles stall the MFMA stream.
+//
+// mainloop_range runs K stages [k0, k0 + KT) of the tile (a stream-K
+// segment); K is the problem's K or, for a segment that ends before it, the
+// segment's end: loads past it fall out of range like loads past the
+// problem's K.
 template <int ES, bool AK, bool BK, class SideWork>
-__device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn,
-                                              int wave, int lane, SideWork& side) {
+__device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, int tm, int tn,
+                                               int wave, int lane, SideWork& side, int k0, int KT,
+                                               int64_t K) {
   typedef StageGeom<ES> G;
   typedef Frags<ES, AK, BK> FW;
   constexpr bool kBf16 = ES == 2;
@@ -454,11 +460,6 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   la.init(a.A, a.a_bytes, a.lda, (int64_t)tm * kTileM, wave, lane);
   lb.init(a.B, a.b_bytes, a.ldb, (int64_t)tn * kTileN, wave, lane);
   const int wm = wave >> 1, wn = wave & 1;
-  int KT = (int)((a.K + G::kK - 1) / G::kK);
-  // Opaque per tile, like the lane ids: tests on KT are then made where they
-  // are used, not once before the tile loop and held (or spilled, and
-  // reloaded with a vmcnt(0)) across it.
-  asm volatile("" : "+s"(KT));
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -470,13 +471,13 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   if (KT > 0) {
     // Prologue: stage 0 and stage 1 in flight (bf16: stage 1's B is loaded in
     // the first iteration), stage 0 certified, its k-step 0 read.
-    la.load_all(0, 0, a.K, wave);
-    lb.load_all(0, kB, a.K, wave);
-    la.load_all(1, kStageBytes, a.K, wave);
+    la.load_all(k0, 0, K, wave);
+    lb.load_all(k0, kB, K, wave);
+    la.load_all(k0 + 1, kStageBytes, K, wave);
     if constexpr (kBf16) {
       wait_vmcnt<8>();
     } else {
-      lb.load_all(1, kStageBytes + kB, a.K, wave);
+      lb.load_all(k0 + 1, kStageBytes + kB, K, wave);
       wait_vmcnt<16>();
     }
     barrier();
@@ -487,8 +488,8 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
     const uint32_t cur = (d & 1) * kStageBytes;
     const uint32_t nxt = ((d + 1) & 1) * kStageBytes;
     int krem_a, krem_b;
-    const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(d + 2, a.K, &krem_a);
-    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(kBf16 ? d + 1 : d + 2, a.K, &krem_b);
+    const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(k0 + d + 2, K, &krem_a);
+    const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(k0 + (kBf16 ? d + 1 : d + 2), K, &krem_b);
     static_for<0, 16>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       sched_fence();
@@ -540,7 +541,7 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   // K tail and the stages past K, which only zero a free slot) keep it.
   // (The two copies of the body must not push anything to scratch: a scratch
   // reload inside the loop waits for every stage load in flight.)
-  int clean = (int)(a.K / G::kK) - 2;
+  int clean = (int)(K / G::kK) - k0 - 2;
   clean = clean < 0 ? 0 : (clean > KT ? KT : clean);
   int d = 0;
   for (; d < clean; ++d) iteration(d, std::integral_constant<bool, false>{});
@@ -551,6 +552,18 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   wait_vmcnt<0>();
   wait_lgkmcnt<0>();
   barrier();
+}
+
+// The whole K loop of one output tile.
+template <int ES, bool AK, bool BK, class SideWork>
+__device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn,
+                                         int wave, int lane, SideWork& side) {
+  int KT = (int)((a.K + StageGeom<ES>::kK - 1) / StageGeom<ES>::kK);
+  // Opaque per tile, like the lane ids: tests on KT are then made where they
+  // are used, not once before the tile loop and held (or spilled, and
+  // reloaded with a vmcnt(0)) across it.
+  asm volatile("" : "+s"(KT));
+  mainloop_range<ES, AK, BK>(acc, a, tm, tn, wave, lane, side, 0, KT, a.K);
 }
 
 }  // namespace migemm

@@ -62,7 +62,17 @@ struct KernelArgs {
   int32_t tiles_m, tiles_n, num_tiles;
   int32_t group_m;     // tile rows per raster group
   int32_t stat_ld;     // ceil(N / 256): leading dimension of row_sum/row_max
-  int32_t pad;
+  // Stream-K (stream-K kernels only; scheduler.hpp): tiles [sk_first,
+  // num_tiles) are cut into K-stage units shared out over the grid.
+  int32_t sk_first;    // first stream-K tile
+  int32_t sk_kt;       // K stages (units) per tile
+  float* sk_partials;  // workspace: kSkPartialSlots fp32 partial tiles per workgroup
+  uint32_t* sk_arrivals;  // workspace: per stream-K tile and wave, zero between runs
 };
+
+// Stream-K workspace: per workgroup, one partial tile for the segment its
+// unit range starts in and one for the segment it ends in.
+constexpr int kSkPartialSlots = 2;
+constexpr int64_t kSkPartialBytes = (int64_t)kTileM * kTileN * 4;  // fp32 tile: 256 KiB
 
 }  // namespace migemm

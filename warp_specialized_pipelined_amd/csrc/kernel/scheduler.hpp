@@ -39,4 +39,21 @@ __device__ __forceinline__ TileCoord tile_of(int L, const KernelArgs& a) {
   return {first_m + r % rows, r / rows};
 }
 
+// Stream-K.  With fewer tiles left than would fill the grid evenly, whole
+// tiles leave compute units idle in the last round (192 tiles on 256 CUs
+// keep 64 idle).  The CUTLASS stream-K scheduler the kernel page selects
+// cuts such tiles into K-stage units instead; here the units of tiles
+// [sk_first, num_tiles), tile after tile, K stage after K stage, are cut
+// into G contiguous ranges, workgroup slot w taking [U w / G, U (w+1) / G).
+// A range covers at most two partial tiles (where it starts and where it
+// ends) and any number of whole ones in between.
+__device__ __forceinline__ int64_t sk_units(const KernelArgs& a) {
+  return (int64_t)(a.num_tiles - a.sk_first) * a.sk_kt;
+}
+__device__ __forceinline__ int64_t sk_begin(int64_t U, int w, int G) { return U * w / G; }
+// The slot whose range holds unit u (the last w with U w / G <= u).
+__device__ __forceinline__ int sk_owner(int64_t U, int64_t u, int G) {
+  return (int)(((u + 1) * G + U - 1) / U) - 1;
+}
+
 }  // namespace migemm

@@ -13,6 +13,7 @@ struct KernelSelect {
   bool a_kmajor;    // A is K-contiguous
   bool b_kmajor;    // B is K-contiguous
   bool consumer;    // tile hand-off + consumer stage
+  bool stream_k;    // stream-K units after the whole tiles (not with consumer)
 };
 
 // Dynamic LDS the selected kernel uses.
@@ -23,5 +24,8 @@ hipError_t prepare_kernel(const KernelSelect& sel);
 
 // Enqueue one persistent GEMM kernel on `stream` with `grid` workgroups.
 hipError_t launch_gemm(const KernelSelect& sel, const KernelArgs& args, int grid, hipStream_t stream);
+
+// Enqueue a kernel that sets n 32-bit words at p to zero.
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
 }  // namespace migemm

@@ -26,12 +26,15 @@ MIGEMM_ERR_LAUNCH = -5
 MIGEMM_ERR_TIMEOUT = -6
 
 MIGEMM_F_TILE_CONSUMER = 0x1
+MIGEMM_F_STREAM_K = 0x2
+MIGEMM_F_STREAM_K_FORCE = 0x4
 MIGEMM_TILE_M = 256
 MIGEMM_TILE_N = 256
 
 EXPORTED = [
     "gemm_desc_validate", "gemm_plan_create", "gemm_plan_destroy", "gemm_plan_get_info",
-    "gemm_plan_workspace_size", "gemm_run", "gemm_run_with_tile_consumer", "gemm_status_string",
+    "gemm_plan_workspace_size", "gemm_workspace_init", "gemm_run", "gemm_run_with_tile_consumer",
+    "gemm_status_string",
 ]
 
 
@@ -57,6 +60,8 @@ class migemm_plan_info(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
         ("swapped", ctypes.c_int32), ("a_kmajor", ctypes.c_int32), ("b_kmajor", ctypes.c_int32),
         ("cu_count", ctypes.c_int32), ("handoff_slots", ctypes.c_int32),
+        ("stream_k_tiles", ctypes.c_int64), ("stream_k_units_per_tile", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -90,6 +95,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_plan_get_info.restype = i32
     lib.gemm_plan_workspace_size.argtypes = [vp]
     lib.gemm_plan_workspace_size.restype = ctypes.c_size_t
+    lib.gemm_workspace_init.argtypes = [vp, vp, vp]
+    lib.gemm_workspace_init.restype = i32
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp]
     lib.gemm_run.restype = i32
     lib.gemm_run_with_tile_consumer.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
@@ -157,6 +164,13 @@ def gemm_plan_workspace_size(plan: int) -> int:
     return int(load().gemm_plan_workspace_size(plan))
 
 
+def gemm_workspace_init(plan, workspace, stream=None, check: bool = True) -> int:
+    st = load().gemm_workspace_init(plan, _ptr(workspace), _stream(stream))
+    if check and st != MIGEMM_OK:
+        raise MigemmError(st, "gemm_workspace_init")
+    return st
+
+
 def gemm_run(plan, A, B, C, D, alpha: float, beta: float, workspace=None, stream=None,
              check: bool = True) -> int:
     st = load().gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha), float(beta),
@@ -184,8 +198,12 @@ class Plan:
         self.handle = gemm_plan_create(desc)
         self.info = gemm_plan_get_info(self.handle)
 
-    def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None):
-        return gemm_run(self.handle, A, B, C, D, alpha, beta, None, stream)
+    @property
+    def workspace_size(self) -> int:
+        return gemm_plan_workspace_size(self.handle)
+
+    def run(self, A, B, C, D, alpha=1.0, beta=0.0, stream=None, workspace=None):
+        return gemm_run(self.handle, A, B, C, D, alpha, beta, workspace, stream)
 
     def run_with_tile_consumer(self, A, B, C, D, alpha, beta, row_sum, row_max, D_copy,
                                stream=None):
