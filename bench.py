@@ -246,6 +246,28 @@ def main():
         extra["fp8_gemm_tflops"] = round(w8.flops / (ms8 * 1e-3) / 1e12, 1)
         extra["fp8_gemm_frac_of_peak"] = round(extra["fp8_gemm_tflops"] / PEAK_FP8_TFLOPS, 4)
         del p8, D8
+        # One GPU's share of an 8-way split of N, 8192 x 1024 x 8192 bf16: 128
+        # tiles on 256 compute units, whole tiles against the stream-K plan.
+        log("[bench] drawing inputs for 8192x1024x8192")
+        g = torch.Generator().manual_seed(81)
+        ps = Problem.random(g, 8192, 1024, 8192, "row", "row", dist="normal").to_device()
+        Ds = ps.new_d(0.0)
+        plan_w = migemm.Plan(ps.desc())
+        plan_s = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_STREAM_K))
+        ws = None
+        if plan_s.workspace_size:
+            ws = torch.empty(plan_s.workspace_size, dtype=torch.uint8, device="cuda")
+            migemm.gemm_workspace_init(plan_s.handle, ws)
+        flops_s = 2.0 * ps.M * ps.N * ps.K
+        n_s, w_s = max(10, args.steps // 2), max(5, args.warmup // 2)
+        ms_w = time_calls(lambda: migemm.gemm_run(plan_w.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0,
+                                                  None, stream), n_s, w_s, stream)
+        ms_s = time_calls(lambda: migemm.gemm_run(plan_s.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0,
+                                                  ws, stream), n_s, w_s, stream)
+        extra["share_8192x1024x8192_whole_tiles_tflops"] = round(flops_s / (ms_w * 1e-3) / 1e12, 1)
+        extra["share_8192x1024x8192_stream_k_tflops"] = round(flops_s / (ms_s * 1e-3) / 1e12, 1)
+        extra["share_8192x1024x8192_stream_k_tiles"] = int(plan_s.info.stream_k_tiles)
+        del ps, Ds, ws
 
     out = {
         "metric": "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 8192^3, fp8) on 1 GPU",
