@@ -91,7 +91,14 @@ typedef enum migemm_status {
  *   - C and D have the same orientation (both row-major or both column-
  *     major); a column-major D is computed as D^T = B^T A^T;
  *   - the tile-consumer flag requires a row-major D;
- *   - the byte span of 256 rows (or K rows) of an operand fits in 2^31.
+ *   - the byte span of 256 rows (or K rows) of an operand fits in 2^31;
+ *   - batches (the pages' rank-4 problem shape, L appended to MNK): L = 0 or
+ *     1 is one product; for L > 1 matrix l of X starts x_bs * l elements
+ *     after X, every x_bs >= 0 and x_bs times the element size a multiple of
+ *     16 bytes; A, B and C may share a matrix between batches (x_bs = 0), D
+ *     may not (d_bs is at least the extent of one D, so batches of D do not
+ *     overlap).  The tile consumer's outputs are per batch too: row_sum and
+ *     row_max are L x M x ceil(N/256), D_copy uses d_bs.
  * c_* fields are ignored when the caller will always pass beta == 0, but
  * must still describe a valid layout (use the same values as D).
  */
@@ -107,6 +114,8 @@ typedef struct migemm_desc {
   int32_t max_workgroups;                 /* 0: one persistent workgroup per CU;
                                              >0: cap on the persistent grid */
   int32_t reserved;                       /* must be 0 */
+  int64_t L;                              /* batch count (0 or 1: one product) */
+  int64_t a_bs, b_bs, c_bs, d_bs;         /* batch strides in elements (L > 1) */
 } migemm_desc;
 
 /* What a plan chose (for tracing and tests). */
@@ -125,6 +134,7 @@ typedef struct migemm_plan_info {
   int64_t stream_k_tiles;  /* tiles cut into K ranges (0: every tile is taken whole) */
   int32_t stream_k_units_per_tile; /* K stages (tile_k each) per such tile */
   int32_t reserved;
+  int64_t batches;         /* L (1 for one product) */
 } migemm_plan_info;
 
 typedef struct migemm_plan migemm_plan; /* opaque, host memory only */

@@ -119,6 +119,20 @@ def test_validation_status_codes(over, status):
     assert migemm.gemm_desc_validate(desc_for(W, **over)) == status
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(L=0), migemm.MIGEMM_OK),                                          # one product
+    (dict(L=3, a_bs=0, b_bs=0, c_bs=0, d_bs=4000 * 3000), migemm.MIGEMM_OK),  # shared A, B, C
+    (dict(L=-1), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(L=2, a_bs=-5000, d_bs=4000 * 3000), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(L=2, d_bs=4000 * 3000 - 8), migemm.MIGEMM_ERR_INVALID_ARG),        # D batches overlap
+    (dict(L=2, a_bs=4, d_bs=4000 * 3000), migemm.MIGEMM_ERR_MISALIGNED),     # 8-byte batch step
+    (dict(L=2, d_bs=4000 * 3000 + 4), migemm.MIGEMM_ERR_MISALIGNED),
+    (dict(L=1 << 24, d_bs=4000 * 3000), migemm.MIGEMM_ERR_UNSUPPORTED),      # 2^31+ tiles
+])
+def test_batch_validation(over, status):
+    assert migemm.gemm_desc_validate(desc_for(W, **over)) == status
+
+
 def test_k_contiguity_rule_only_applies_to_k_contiguous_operands():
     # A column-major (M-contiguous) and B row-major (N-contiguous): any K is fine
     d = migemm.make_desc(64, 64, 17, 1, 1, 1, 64, 64, 1, 64, 1, 64, 1)

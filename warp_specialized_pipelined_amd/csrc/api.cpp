@@ -69,6 +69,8 @@ struct Canon {
   int64_t M, N, K;
   int64_t a_rs, a_cs, b_rs, b_cs, c_rs, c_cs, d_rs, d_cs;
   bool swapped;
+  int64_t L;                       // batches (>= 1)
+  int64_t a_bs, b_bs, c_bs, d_bs;  // batch strides in elements (0 when L == 1)
 };
 
 int validate(const migemm_desc* d, Canon* out) {
@@ -97,15 +99,28 @@ int validate(const migemm_desc* d, Canon* out) {
   // A K-contiguous operand is fetched in 16-byte chunks along K.
   const bool a_k = oa.row_major, b_k = !ob.row_major;
   if ((a_k || b_k) && (d->K * es) % 16) return MIGEMM_ERR_MISALIGNED;
+  // Batches: non-negative strides keeping every matrix 16-byte aligned; the
+  // batches of D must not overlap (A, B and C may be shared).
+  if (d->L < 0) return MIGEMM_ERR_INVALID_ARG;
+  const int64_t L = d->L > 1 ? d->L : 1;
+  int64_t a_bs = 0, b_bs = 0, c_bs = 0, d_bs = 0;
+  if (L > 1) {
+    a_bs = d->a_bs, b_bs = d->b_bs, c_bs = d->c_bs, d_bs = d->d_bs;
+    if (a_bs < 0 || b_bs < 0 || c_bs < 0 || d_bs < 0) return MIGEMM_ERR_INVALID_ARG;
+    if (d->M > 0 && d->N > 0 && d_bs * 2 < extent_bytes(d->M, d->N, d->d_rs, d->d_cs, 2))
+      return MIGEMM_ERR_INVALID_ARG;
+    if ((a_bs * es) % 16 || (b_bs * es) % 16 || (c_bs * 2) % 16 || (d_bs * 2) % 16)
+      return MIGEMM_ERR_MISALIGNED;
+  }
 
   Canon c;
   if (od.row_major) {
     c = {d->M, d->N, d->K, d->a_rs, d->a_cs, d->b_rs, d->b_cs,
-         d->c_rs, d->c_cs, d->d_rs, d->d_cs, false};
+         d->c_rs, d->c_cs, d->d_rs, d->d_cs, false, L, a_bs, b_bs, c_bs, d_bs};
   } else {
     // D^T = B^T A^T: swap the roles of A and B and transpose every operand.
     c = {d->N, d->M, d->K, d->b_cs, d->b_rs, d->a_cs, d->a_rs,
-         d->c_cs, d->c_rs, d->d_cs, d->d_rs, true};
+         d->c_cs, d->c_rs, d->d_cs, d->d_rs, true, L, b_bs, a_bs, c_bs, d_bs};
   }
   // 32-bit buffer offsets: 256 rows of a K-contiguous operand, or one stage
   // of K rows of an MN-contiguous one (128 bytes of K: 64 bf16 or 128 e4m3
@@ -124,6 +139,10 @@ int validate(const migemm_desc* d, Canon* out) {
     return MIGEMM_ERR_UNSUPPORTED;
   if (c.M / migemm::kTileM >= (1 << 20) || c.N / migemm::kTileN >= (1 << 20))
     return MIGEMM_ERR_UNSUPPORTED;
+  // Tile indices are 32-bit.
+  const int64_t tiles = ((c.M + migemm::kTileM - 1) / migemm::kTileM) *
+                        ((c.N + migemm::kTileN - 1) / migemm::kTileN);
+  if (tiles > 0 && L > (int64_t)0x7FFFFFFF / tiles) return MIGEMM_ERR_UNSUPPORTED;
   if (out) *out = c;
   return MIGEMM_OK;
 }
@@ -203,7 +222,12 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   a.b_bytes = extent_bytes(c.K, c.N, c.b_rs, c.b_cs, es);
   a.tiles_m = (int32_t)((c.M + migemm::kTileM - 1) / migemm::kTileM);
   a.tiles_n = (int32_t)((c.N + migemm::kTileN - 1) / migemm::kTileN);
-  a.num_tiles = a.tiles_m * a.tiles_n;
+  a.tiles_per_batch = a.tiles_m * a.tiles_n;
+  a.num_tiles = (int32_t)(c.L * a.tiles_per_batch);
+  a.a_bs_bytes = c.a_bs * es;
+  a.b_bs_bytes = c.b_bs * es;
+  a.c_bs_bytes = c.c_bs * 2;
+  a.d_bs_bytes = c.d_bs * 2;
   a.group_m = a.tiles_m < 8 ? (a.tiles_m > 0 ? a.tiles_m : 1) : 8;
   a.stat_ld = a.tiles_n;
 
@@ -282,6 +306,8 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
   out->handoff_slots = migemm::kHandoffSlots;
   out->stream_k_tiles = p->sel.stream_k ? p->base.num_tiles - p->base.sk_first : 0;
   out->stream_k_units_per_tile = p->sel.stream_k ? p->base.sk_kt : 0;
+  out->batches = p->base.tiles_per_batch > 0 ? p->base.num_tiles / p->base.tiles_per_batch
+                                             : (p->desc.L > 1 ? p->desc.L : 1);
   return MIGEMM_OK;
 }
 

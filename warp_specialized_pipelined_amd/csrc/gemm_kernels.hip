@@ -43,10 +43,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     const int whole = SK ? a.sk_first : a.num_tiles;  // tiles taken whole
     for (int L = first; L < whole; L += gridDim.x) {
       const TileCoord t = tile_of(L, a);
+      const KernelArgs ab = batch_args(a, t.l);
       const LaneIds id(lane, wave);
-      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none);
+      mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
       const LaneIds ie(lane, wave);
-      epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
+      epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
       wait_lgkmcnt<0>();  // staging reads done ...
       barrier();          // ... in every wave before the ring is refilled
     }
@@ -62,14 +63,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     int n = 0;
     for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
       const TileCoord t = tile_of(L, a);
+      const KernelArgs ab = batch_args(a, t.l);
       if (n > 0) cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
       const LaneIds id(lane, wave);
-      mainloop<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, cons);
+      mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, cons);
       cons.drain(a, wave, lane);
       const int s = n % kHandoffSlots;
       HandoffRing::acquire(s, n / kHandoffSlots);
       const LaneIds ie(lane, wave);
-      epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
+      epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
       HandoffRing::commit(s, L, wave, lane);
       wait_lgkmcnt<0>();
       barrier();

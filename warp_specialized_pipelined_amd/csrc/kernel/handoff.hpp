@@ -219,6 +219,7 @@ struct TileConsumer {
     slot = slot_;
     const int tile_id = uni(HandoffRing::wait(slot, use));
     const TileCoord t = tile_of(tile_id, a);
+    const KernelArgs ab = batch_args(a, t.l);
     const int64_t r0 = (int64_t)t.tm * kTileM;
     const int64_t c0 = (int64_t)t.tn * kTileN;
     const int64_t rleft = a.M - r0, cleft = a.N - c0;
@@ -229,10 +230,12 @@ struct TileConsumer {
     int64_t bytes = ((a.M - 1 - r0) * a.ldd + (a.N - c0)) * 2;
     bytes = (bytes + 15) & ~(int64_t)15;  // per-dword range checks: see StageLoader::stage_rsrc
     const uint32_t nb = (uint32_t)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
-    src = make_rsrc(static_cast<const unsigned short*>(a.D) + r0 * a.ldd + c0, nb);
-    cpy = make_rsrc(static_cast<const unsigned short*>(a.D_copy) + r0 * a.ldd + c0, nb);
-    const int64_t s0 = r0 * a.stat_ld + t.tn;
-    int64_t sbytes = (a.M * (int64_t)a.stat_ld - s0) * 4;
+    src = make_rsrc(static_cast<const unsigned short*>(ab.D) + r0 * a.ldd + c0, nb);
+    cpy = make_rsrc(static_cast<const unsigned short*>(ab.D_copy) + r0 * a.ldd + c0, nb);
+    // Statistics of batch l: rows l*M .. l*M + M-1 of an (L*M) x stat_ld array.
+    const int64_t srow0 = (int64_t)t.l * a.M + r0;
+    const int64_t s0 = srow0 * a.stat_ld + t.tn;
+    int64_t sbytes = ((int64_t)t.l * a.M + a.M) * a.stat_ld * 4 - s0 * 4;
     sbytes = sbytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : sbytes;
     rsum = make_rsrc(a.row_sum + s0, (uint32_t)sbytes);
     rmax = make_rsrc(a.row_max + s0, (uint32_t)sbytes);

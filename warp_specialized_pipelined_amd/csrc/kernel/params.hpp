@@ -68,6 +68,11 @@ struct KernelArgs {
   int32_t sk_kt;       // K stages (units) per tile
   float* sk_partials;  // workspace: kSkPartialSlots fp32 partial tiles per workgroup
   uint32_t* sk_arrivals;  // workspace: per stream-K tile and wave, zero between runs
+  // Batches: tiles are numbered batch after batch (tiles_per_batch each);
+  // matrix l of an operand starts l * stride bytes after its pointer.
+  int32_t tiles_per_batch;
+  int32_t pad2;
+  int64_t a_bs_bytes, b_bs_bytes, c_bs_bytes, d_bs_bytes;
 };
 
 // Stream-K workspace: per workgroup, one partial tile for the segment its

@@ -25,18 +25,34 @@ __device__ __forceinline__ int persistent_slot(int bid, int grid) {
 
 struct TileCoord {
   int tm, tn;
+  int l;  // batch
 };
 
-// Logical tile index -> (tile row, tile column).  Tiles are taken in groups
-// of `group_m` tile rows; inside a group they run down the columns, so that
-// consecutive indices share the B panel and nearby ones share A panels.
+// Logical tile index -> (tile row, tile column, batch).  Batches come one
+// after another.  Inside one, tiles are taken in groups of `group_m` tile
+// rows, running down the columns inside a group, so that consecutive indices
+// share the B panel and nearby ones share A panels.
 __device__ __forceinline__ TileCoord tile_of(int L, const KernelArgs& a) {
+  const int l = L / a.tiles_per_batch;
+  L -= l * a.tiles_per_batch;
   const int per_group = a.group_m * a.tiles_n;
   const int g = L / per_group;
   const int first_m = g * a.group_m;
   const int rows = min(a.tiles_m - first_m, a.group_m);
   const int r = L - g * per_group;
-  return {first_m + r % rows, r / rows};
+  return {first_m + r % rows, r / rows, l};
+}
+
+// The arguments as batch l sees them: every operand pointer moved to its
+// matrix of that batch, so the K loop and the epilogue work on one product.
+__device__ __forceinline__ KernelArgs batch_args(const KernelArgs& a, int l) {
+  KernelArgs b = a;
+  b.A = static_cast<const unsigned char*>(a.A) + l * a.a_bs_bytes;
+  b.B = static_cast<const unsigned char*>(a.B) + l * a.b_bs_bytes;
+  if (a.C) b.C = static_cast<const unsigned char*>(a.C) + l * a.c_bs_bytes;
+  b.D = static_cast<unsigned char*>(a.D) + l * a.d_bs_bytes;
+  if (a.D_copy) b.D_copy = static_cast<unsigned char*>(a.D_copy) + l * a.d_bs_bytes;
+  return b;
 }
 
 // Stream-K.  With fewer tiles left than would fill the grid evenly, whole

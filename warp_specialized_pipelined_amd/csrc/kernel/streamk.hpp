@@ -140,6 +140,7 @@ __device__ __forceinline__ void stream_k_tiles(Accum& acc, const KernelArgs& a, 
     const int kb = (int)(u - (int64_t)s * kt);
     const int n = (int)((int64_t)(kt - kb) < u1 - u ? (int64_t)(kt - kb) : u1 - u);
     const TileCoord t = tile_of(a.sk_first + s, a);
+    const KernelArgs ab = batch_args(a, t.l);
     // A segment that ends before the tile's last stage ends the K range
     // there: its loads past it fall out of range.
     const int64_t kend_stage = (int64_t)(kb + n) * StageGeom<ES>::kK;
@@ -147,11 +148,11 @@ __device__ __forceinline__ void stream_k_tiles(Accum& acc, const KernelArgs& a, 
     int k0 = kb, nk = n;
     asm volatile("" : "+s"(k0), "+s"(nk));
     const SkIds id(lane, wave);
-    mainloop_range<ES, AK, BK>(acc, a, t.tm, t.tn, id.wave, id.lane, none, k0, nk, kend);
+    mainloop_range<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none, k0, nk, kend);
     const SkIds ie(lane, wave);
     bool finish = n == kt;
     if (!finish) finish = stream_k_fixup(acc, a, s, w, G, U, ie.wave, ie.lane);
-    if (finish) epilogue_store(acc, a, t.tm, t.tn, ie.wave, ie.lane);
+    if (finish) epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
     wait_lgkmcnt<0>();  // staging reads done ...
     barrier();          // ... in every wave before the ring is refilled
     u += n;

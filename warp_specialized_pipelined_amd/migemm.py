@@ -49,6 +49,9 @@ class migemm_desc(ctypes.Structure):
         ("d_rs", ctypes.c_int64), ("d_cs", ctypes.c_int64),
         ("device", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("max_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("L", ctypes.c_int64),
+        ("a_bs", ctypes.c_int64), ("b_bs", ctypes.c_int64),
+        ("c_bs", ctypes.c_int64), ("d_bs", ctypes.c_int64),
     ]
 
 
@@ -61,7 +64,7 @@ class migemm_plan_info(ctypes.Structure):
         ("swapped", ctypes.c_int32), ("a_kmajor", ctypes.c_int32), ("b_kmajor", ctypes.c_int32),
         ("cu_count", ctypes.c_int32), ("handoff_slots", ctypes.c_int32),
         ("stream_k_tiles", ctypes.c_int64), ("stream_k_units_per_tile", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("batches", ctypes.c_int64),
     ]
 
 
@@ -126,9 +129,10 @@ def _stream(s) -> int | None:
 
 
 def make_desc(M, N, K, a_type, b_type, a_rs, a_cs, b_rs, b_cs, c_rs, c_cs, d_rs, d_cs,
-              device=0, flags=0, max_workgroups=0, c_type=MIGEMM_BF16, d_type=MIGEMM_BF16):
+              device=0, flags=0, max_workgroups=0, c_type=MIGEMM_BF16, d_type=MIGEMM_BF16,
+              L=1, a_bs=0, b_bs=0, c_bs=0, d_bs=0):
     return migemm_desc(M, N, K, a_type, b_type, c_type, d_type, a_rs, a_cs, b_rs, b_cs, c_rs, c_cs,
-                       d_rs, d_cs, device, flags, max_workgroups, 0)
+                       d_rs, d_cs, device, flags, max_workgroups, 0, L, a_bs, b_bs, c_bs, d_bs)
 
 
 def gemm_status_string(status: int) -> str:
