@@ -56,25 +56,41 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
   const uint32_t st_base = wave * kStagingWaveBytes + lr * kStagingRowBytes + 8 * half;
 
   if (a.beta != 0.0f) {
+    // C of the wave's quarter lands in the wave's staging area, already in
+    // the staging layout (rows of kStagingRowBytes, the last 16 bytes of
+    // each unused), through LDS-DMA: lane i of load j fills bytes
+    // 1024 j + 16 i, so it fetches the 16 bytes of C that belong there.
+    // Whole row segments per instruction, instead of 8-byte pieces of 32
+    // rows.  Out-of-range C reads return 0 or land in columns >= N; either
+    // way they only feed outputs that are never stored.
     const __amdgpu_buffer_rsrc_t rc = matrix_rsrc(a.C, a.ldc, a.M, a.N, m0, n0, true);
-    const uint32_t c_lane = (uint32_t)((lr * a.ldc + 4 * half) * 2);
+    const uint32_t wave_base = wave * kStagingWaveBytes;
+    wait_lgkmcnt<0>();  // earlier reads of this area (the consumer's drain) are done
+    static_assert(kStagingWaveBytes % 1024 == 0, "whole LDS-DMA loads per wave");
+#pragma unroll
+    for (int j = 0; j < kStagingWaveBytes / 1024; ++j) {
+      const int b = 1024 * j + 16 * lane;
+      const int row = b / kStagingRowBytes;
+      const int off = b - row * kStagingRowBytes;
+      dma16_w5_nt(rc, lds_at(wave_base + 1024 * j),
+                  off < kWaveTile * 2 ? (uint32_t)(row * a.ldc * 2 + off) : kOobOffset);
+    }
+    wait_vmcnt<0>();
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
-      const uint32_t c_row = c_lane + (uint32_t)(32 * bi * a.ldc * 2);
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // Out-of-range C reads return 0 or land in columns >= N; either way
-          // they only feed outputs that are never stored.
-          const u32x2 cw = __builtin_amdgcn_raw_buffer_load_b64(rc, c_row + (32 * bj + 8 * q) * 2, 0, 0);
+          const uint32_t at = st_base + 32 * bi * kStagingRowBytes + (4 * bj + q) * 16;
+          const u32x2 cw = *(const MIGEMM_LDS u32x2*)lds_at(at);
           const f32x16& r = acc.v[bi][bj];
           const float v0 = a.alpha * r[4 * q + 0] + a.beta * bf16_lo(cw[0]);
           const float v1 = a.alpha * r[4 * q + 1] + a.beta * bf16_hi(cw[0]);
           const float v2 = a.alpha * r[4 * q + 2] + a.beta * bf16_lo(cw[1]);
           const float v3 = a.alpha * r[4 * q + 3] + a.beta * bf16_hi(cw[1]);
           const u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *(MIGEMM_LDS u32x2*)lds_at(st_base + 32 * bi * kStagingRowBytes + (4 * bj + q) * 16) = w;
+          *(MIGEMM_LDS u32x2*)lds_at(at) = w;  // over the C it was formed from
         }
       }
     }
