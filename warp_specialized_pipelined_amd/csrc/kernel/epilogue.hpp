@@ -21,8 +21,10 @@
 //     constant, so it folds into the instruction's offset field;
 //   - read back, one ds_read_b128 per lane covers 4 full 256-byte rows, which
 //     leave as coalesced 16-byte buffer stores.
-// C (when beta != 0) is read in the accumulator layout, 8 bytes per lane, so
-// that alpha*acc + beta*C is formed in fp32 and rounded once.
+// C (when beta != 0) first lands in the wave's staging area, in the staging
+// layout, through LDS-DMA loads of whole row segments; each lane then reads
+// its 8 bytes of C at the place its result goes, so alpha*acc + beta*C is
+// formed in fp32, rounded once, and written over that C.
 #pragma once
 
 #include "gfx950.hpp"
