@@ -89,6 +89,21 @@ def test_stream_k_shapes(M, N, K, mw, beta):
     assert_same_bits(outs)
 
 
+def test_stream_k_partials_cross_xcds_bitwise_over_runs():
+    # 64 tiles of 64 stages on every compute unit: 4 contributors per tile,
+    # spread over XCDs with private L2s.  A partial read before its writer's
+    # stores were visible would change the sum, so 20 runs must agree bit
+    # for bit (and the first must pass the oracle).
+    g = torch.Generator().manual_seed(64)
+    p = Problem.random(g, 2048, 2048, 4096, "row", "row", dist="normal").to_device()
+    plan, ws = sk_plan(p)
+    assert plan.info.stream_k_tiles == 64 and plan.info.grid == plan.info.cu_count
+    outs = sk_runs(p, plan, ws, runs=20)
+    r = check_sampled(p, outs[0], n_random=4096, seed=64)
+    assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, r
+    assert_same_bits(outs)
+
+
 def test_stream_k_layouts_and_fp8():
     g = torch.Generator().manual_seed(23)
     cases = [("col", "col", synth.BF16, "row"), ("row", "col", synth.E4M3, "row"),
