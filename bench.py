@@ -231,6 +231,17 @@ def main():
         extra["plain_gemm_frac_of_peak"] = round(extra["plain_gemm_tflops"] / PEAK_BF16_TFLOPS, 4)
         if consumer:
             extra["consumer_over_plain_time"] = round(ms / ms_plain, 4)
+        # The vendor library on the same inputs, for reference only: torch's
+        # bf16 matmul (hipBLASLt) of the same row-major A and B, contiguous.
+        if p.a_rs == w.K and p.b_rs == w.N and p.a_cs == 1 and p.b_cs == 1:
+            A2 = p.dA.view(w.M, w.K)
+            B2 = p.dB.view(w.K, w.N)
+            out2 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+            ms_lib = time_calls(lambda: torch.matmul(A2, B2, out=out2), max(10, args.steps // 2),
+                                max(5, args.warmup // 2), stream)
+            extra["library_gemm_tflops"] = round(w.flops / (ms_lib * 1e-3) / 1e12, 1)
+            extra["library_gemm"] = "torch.matmul bf16 (hipBLASLt), same A and B, no consumer"
+            del out2
         # fp8 e4m3 8192 x 8192 x 16384
         w8 = synth.WORKLOADS[4]
         log(f"[bench] drawing inputs for {w8.name}")
