@@ -59,34 +59,53 @@ __device__ __forceinline__ int sk_which(int64_t U, int c, int G, int64_t tu0) {
   return sk_begin(U, c, G) >= tu0 ? 0 : 1;
 }
 
-// A partial segment of stream-K tile s is done: publish it.  If this wave is
-// the tile's last arrival for its quarter, add all partials into acc and
-// return true (the caller then stores the quarter).
+
+// A partial segment of stream-K tile s is done.  If this wave finishes the
+// tile's quarter, add all partials into acc and return true (the caller then
+// stores the quarter); otherwise publish the partial and return false.
+//
+// The contributor holding the tile's K stage 0 (the head, w_lo) often gets
+// here last: when its range started in an earlier tile, this segment ends
+// its range while the others run theirs first in theirs.  So the head looks
+// at the counter once; if all the others have counted in, it takes their
+// partials without storing its own.  Otherwise it publishes its partial like
+// every other contributor and the last arrival finishes the tile.  Either
+// way exactly one wave finishes, and nobody waits.
 __device__ __forceinline__ bool stream_k_fixup(Accum& acc, const KernelArgs& a, int s, int w,
                                                int G, int64_t U, int wave, int lane) {
   const int64_t tu0 = (int64_t)s * a.sk_kt;
   const int w_lo = sk_owner(U, tu0, G);
   const int w_hi = sk_owner(U, tu0 + a.sk_kt - 1, G);
-
-  const __amdgpu_buffer_rsrc_t mine = sk_slot(a, w, sk_which(U, w, G, tu0), wave);
-#pragma unroll
-  for (int b = 0; b < 16; ++b)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& v = acc.v[b >> 2][b & 3];
-      const f32x4 piece = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, piece), mine,
-                                             sk_piece(b, q, lane), 0, kCpolDevice);
-    }
-  // Release: every partial store has completed before the arrival counts.
-  compiler_fence();
-  wait_vmcnt<0>();
-  compiler_fence();
+  const uint32_t others = (uint32_t)(w_hi - w_lo);
   uint32_t* counter = a.sk_arrivals + (int64_t)s * kWaves + wave;
-  uint32_t before = 0;
-  if (lane == 0) before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  before = __builtin_amdgcn_readfirstlane(before);
-  if (before != (uint32_t)(w_hi - w_lo)) return false;  // not the last contributor
+
+  bool head_done = false;
+  if (w == w_lo) {
+    uint32_t seen = 0;
+    if (lane == 0) seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    head_done = __builtin_amdgcn_readfirstlane(seen) == others;
+  }
+  if (!head_done) {
+    const __amdgpu_buffer_rsrc_t mine = sk_slot(a, w, sk_which(U, w, G, tu0), wave);
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& v = acc.v[b >> 2][b & 3];
+        const f32x4 piece = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, piece), mine,
+                                               sk_piece(b, q, lane), 0, kCpolDevice);
+      }
+    // Release: every partial store has completed before the arrival counts.
+    compiler_fence();
+    wait_vmcnt<0>();
+    compiler_fence();
+    uint32_t before = 0;
+    if (lane == 0) before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The last of all contributors finishes.  (When the head finished
+    // without counting in, the others' counts stop one short of this.)
+    if (__builtin_amdgcn_readfirstlane(before) != others) return false;
+  }
 
   // Acquire: the loads below come after the count they depend on.
   compiler_fence();
