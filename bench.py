@@ -134,6 +134,82 @@ def time_calls(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps   # ms per call
 
 
+def sysfs_gpu_dir():
+    """The sysfs directory of GPU 0 (by its PCI address when torch reports
+    one, else the only amdgpu card present), or None."""
+    import glob
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    bus = getattr(prop, "pci_bus_id", None)
+    if bus is not None:
+        d = f"/sys/bus/pci/devices/{getattr(prop, 'pci_domain_id', 0):04x}:{bus:02x}:" \
+            f"{getattr(prop, 'pci_device_id', 0):02x}.0"
+        if os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+            return d
+    cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return os.path.dirname(cards[0]) if len(cards) == 1 else None
+
+
+def read_sclk_mhz(path):
+    """Current shader clock from amdgpu's pp_dpm_sclk: the level marked '*'."""
+    with open(path) as f:
+        for line in f:
+            if line.rstrip().endswith("*"):
+                return float(line.split(":")[1].strip().split("M")[0])
+    return None
+
+
+def observe_clock(step, stream, ms_per_step, seconds=1.5, period=0.01):
+    """Run `step` back to back for about `seconds` while a thread samples the
+    shader clock (and the board power, where hwmon reports it) every
+    `period` s.  Returns the median clock, the throughput of that run and
+    the sample counts; None where the driver exposes nothing."""
+    import glob
+    import statistics
+    import threading
+    import torch
+    d = sysfs_gpu_dir()
+    if d is None:
+        return None
+    sclk_path = os.path.join(d, "pp_dpm_sclk")
+    pw = sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_average")) +
+                glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_input")))
+    clocks, watts, stop = [], [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                c = read_sclk_mhz(sclk_path)
+                if c is not None:
+                    clocks.append(c)
+                if pw:
+                    with open(pw[0]) as f:
+                        watts.append(int(f.read()) / 1e6)
+            except (OSError, ValueError, IndexError):
+                pass
+            time.sleep(period)
+
+    n = max(10, int(seconds * 1e3 / ms_per_step))
+    torch.cuda.synchronize()
+    t = threading.Thread(target=sample, daemon=True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(n):
+        step()
+        if i == n // 10:
+            t.start()               # sample once the run is under way
+    end.record(stream)
+    torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    if not clocks:
+        return None
+    return {"sclk_mhz": statistics.median(clocks), "sclk_samples": len(clocks),
+            "watts": statistics.median(watts) if watts else None,
+            "ms": start.elapsed_time(end) / n, "steps": n}
+
+
 def cpu_baseline(p, target_s):
     """Time the oracle on the first R rows of the workload (all N columns,
     full K), R chosen so the run takes about target_s seconds."""
@@ -224,6 +300,25 @@ def main():
     log(f"[bench] {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  ({wall:.1f} s wall)")
 
     extra = {"consumer_variant": consumer}
+
+    def clock_extras(prefix, fn, ms_step, flops, flop_per_clk_cu):
+        """The shader clock under this load (amdgpu's DPM readout), the board
+        power, and the throughput as a fraction of the MFMA peak at that
+        clock: context for the nominal fraction, which prices every cycle at
+        2.4 GHz."""
+        clk = observe_clock(fn, stream, ms_step)
+        log(f"[bench] clock run {prefix}: {clk}")
+        if clk is None:
+            return
+        t_clk = flops / (clk["ms"] * 1e-3) / 1e12
+        extra[prefix + "sclk_mhz_median"] = clk["sclk_mhz"]
+        extra[prefix + "tflops_during_clock_run"] = round(t_clk, 1)
+        extra[prefix + "frac_of_peak_at_observed_sclk"] = round(
+            t_clk / (256 * clk["sclk_mhz"] * 1e6 * flop_per_clk_cu / 1e12), 4)
+        if clk["watts"] is not None:
+            extra[prefix + "board_power_w_median"] = round(clk["watts"], 1)
+
+    clock_extras("", step, ms, w.flops, 4096)
     if not args.no_extra:
         ms_plain = time_calls(step_plain, args.steps, max(2, args.warmup // 2), stream)
         extra["plain_gemm_ms"] = round(ms_plain, 4)
@@ -231,6 +326,7 @@ def main():
         extra["plain_gemm_frac_of_peak"] = round(extra["plain_gemm_tflops"] / PEAK_BF16_TFLOPS, 4)
         if consumer:
             extra["consumer_over_plain_time"] = round(ms / ms_plain, 4)
+            clock_extras("plain_gemm_", step_plain, ms_plain, w.flops, 4096)
         # The vendor library on the same inputs, for reference only: torch's
         # bf16 matmul (hipBLASLt) of the same row-major A and B, contiguous.
         if p.a_rs == w.K and p.b_rs == w.N and p.a_cs == 1 and p.b_cs == 1:
@@ -241,6 +337,8 @@ def main():
                                 max(5, args.warmup // 2), stream)
             extra["library_gemm_tflops"] = round(w.flops / (ms_lib * 1e-3) / 1e12, 1)
             extra["library_gemm"] = "torch.matmul bf16 (hipBLASLt), same A and B, no consumer"
+            clock_extras("library_gemm_", lambda: torch.matmul(A2, B2, out=out2), ms_lib, w.flops,
+                         4096)
             del out2
         # fp8 e4m3 8192 x 8192 x 16384
         w8 = synth.WORKLOADS[4]
@@ -256,6 +354,7 @@ def main():
         extra["fp8_gemm_ms"] = round(ms8, 4)
         extra["fp8_gemm_tflops"] = round(w8.flops / (ms8 * 1e-3) / 1e12, 1)
         extra["fp8_gemm_frac_of_peak"] = round(extra["fp8_gemm_tflops"] / PEAK_FP8_TFLOPS, 4)
+        clock_extras("fp8_gemm_", step8, ms8, w8.flops, 8192)
         del p8, D8
         # One GPU's share of an 8-way split of N, 8192 x 1024 x 8192 bf16: 128
         # tiles on 256 compute units, whole tiles against the stream-K plan.
