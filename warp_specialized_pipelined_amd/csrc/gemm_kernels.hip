@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
   } else {
     // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
     // The consumer stage of tile n runs inside tile n+1's K loop; the last
-    // tile's runs after the loop.
+    // tile's runs after the loop, on the tile as its epilogue staged it.
     HandoffRing::init();
     __syncthreads();
     TileConsumer cons;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     }
     if (n > 0) {
       cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
-      cons.drain(a, wave, lane);
+      cons.drain_staged(wave, lane);
     }
   }
 }

@@ -273,10 +273,14 @@ struct TileConsumer {
   // Read step `folded` back from LDS at `slot` (its fetch must have
   // completed).
   __device__ __forceinline__ void read_back_at(uint32_t slot, int lane) {
+    read_back_lane(slot + 16 * lane);
+  }
+  // Same, from this lane's own LDS address.
+  __device__ __forceinline__ void read_back_lane(uint32_t at) {
     compiler_fence();
     fold_j = uni(folded);
     folded = fold_j + 1;
-    v = *(const MIGEMM_LDS u32x4*)lds_at(slot + 16 * lane);
+    v = *(const MIGEMM_LDS u32x4*)lds_at(at);
     folding = true;
   }
   __device__ __forceinline__ void read_back(int wave, int lane) {
@@ -392,6 +396,35 @@ struct TileConsumer {
     if (!uni(active)) return;
     if (uni(fetched) > uni(folded)) read_back(wave, lane);
     if (uni(fetched) < kSteps) fetch(wave);
+  }
+
+  // Where the epilogue left this lane's 16 bytes of step j: wave q staged
+  // the quarter of rows 128 (q / 2) .. + 127 and columns 128 (q % 2) .. +
+  // 127, row by row at kStagingRowBytes.
+  __device__ __forceinline__ static uint32_t staged_at(int wave, int lane, int j) {
+    const int row = wave * 64 + 2 * j + (lane >> 5);
+    const int col = 8 * (lane & 31);
+    const int q = 2 * (row >> 7) + (col >> 7);
+    return q * kStagingWaveBytes + (row & 127) * kStagingRowBytes + (col & 127) * 2;
+  }
+
+  // The last tile of the workgroup, after its epilogue: the tile is still
+  // staged in LDS (every wave staged its quarter there, and no K loop
+  // follows to overwrite it), so every step is read there instead of being
+  // fetched back from D -- at the kernel's end, when every compute unit
+  // drains at once and the fetches would queue for memory together.  The
+  // bytes are the ones the epilogue stored to D.  The wait in begin() saw
+  // all four waves commit, which orders their staging writes before these
+  // reads.
+  __device__ __forceinline__ void drain_staged(int wave, int lane) {
+    asm volatile("" : "+v"(lane));  // (as in begin)
+    while (uni(active)) {
+      read_back_lane(staged_at(wave, lane, uni(folded)));
+      compute<0>(lane);
+      compute<1>(lane);
+      compute<2>(lane);
+      store_pending(lane);
+    }
   }
 
   // After the K loop: the steps the loop did not finish.  The ring and this
