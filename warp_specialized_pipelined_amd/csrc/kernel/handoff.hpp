@@ -15,7 +15,7 @@
 // The payload is the tile itself, already stored in D.  The counters only
 // grow, so no phase bit is needed: the u-th use of a slot (u = 0, 1, ...)
 //   acquire  waits for  empty >= u * kWaves      (passes at once for u = 0)
-//   commit   adds 1 to  full    (each producer wave, after its stores landed)
+//   commit   adds 1 to  full    (each producer wave, its stores ordered before)
 //   wait     waits for  full  >= (u + 1) * kWaves
 //   release  adds 1 to  empty   (each consumer wave, after its reads landed)
 // Every wave is both a producer (its quarter of the tile) and a consumer (64
@@ -62,7 +62,9 @@ struct HandoffRing {
     spin_until(word(slot, kEmpty), use * kWaves);
   }
   // Publishes the caller's stores of the tile: the workgroup-scope release
-  // fence waits for them to complete before the count goes up.
+  // fence orders them before the count.  (The waves of a workgroup share
+  // the compute unit's path to memory, so outside tgsplit mode this fence
+  // compiles to no wait at all: the stores may still be in flight.)
   __device__ __forceinline__ static void commit(int slot, int tile_id, int wave, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) {
