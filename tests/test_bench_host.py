@@ -1,0 +1,45 @@
+"""Host-side pieces of bench.py (CPU): the shader-clock readout parser, the
+traffic gate, and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def write(tmp_path, text):
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text(text)
+    return str(p)
+
+
+def test_sclk_readout_takes_the_level_marked_current(tmp_path):
+    # amdgpu lists the DPM levels one a line and marks the current one with
+    # '*'; when the clock sits between levels an extra 'S:' line carries it.
+    assert bench.read_sclk_mhz(write(tmp_path, "S: 98Mhz *\n0: 500Mhz\n1: 2400Mhz\n")) == 98.0
+    assert bench.read_sclk_mhz(write(tmp_path, "0: 500Mhz\n1: 2400Mhz *\n")) == 2400.0
+    assert bench.read_sclk_mhz(write(tmp_path, "0: 500Mhz\nS: 1801Mhz *\n1: 2400Mhz\n")) == 1801.0
+    assert bench.read_sclk_mhz(write(tmp_path, "0: 500Mhz\n1: 2400Mhz\n")) is None
+
+
+def test_traffic_is_reported_only_for_the_profiled_kernel(tmp_path, monkeypatch):
+    # The committed counter profile carries the hash of the kernel sources
+    # it was taken with; a profile of other sources gives null traffic.
+    prof = tmp_path / "traffic.txt"
+    prof.write_text(f"kernel_source_sha1: {bench.kernel_source_hash()}\nhbm_bytes_per_launch: 123\n")
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
+    assert bench.measured_traffic() == 123
+    prof.write_text("kernel_source_sha1: 0000\nhbm_bytes_per_launch: 123\n")
+    assert bench.measured_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "missing.txt"))
+    assert bench.measured_traffic() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""   # no JSON line: nothing was measured
