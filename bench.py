@@ -327,6 +327,15 @@ def main():
         if consumer:
             extra["consumer_over_plain_time"] = round(ms / ms_plain, 4)
             clock_extras("plain_gemm_", step_plain, ms_plain, w.flops, 4096)
+            # The other schedule of the consumer stage: inside the next
+            # tile's K loop, on the tile fetched back from D.
+            plan_ov = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER |
+                                         migemm.MIGEMM_F_CONSUMER_OVERLAP))
+            ms_ov = time_calls(lambda: migemm.gemm_run_with_tile_consumer(
+                plan_ov.handle, p.dA, p.dB, None, D, p.alpha, 0.0, row_sum, row_max, D_copy, None,
+                stream), args.steps, max(2, args.warmup // 2), stream)
+            extra["consumer_overlapped_tflops"] = round(w.flops / (ms_ov * 1e-3) / 1e12, 1)
+            extra["consumer_overlapped_over_plain_time"] = round(ms_ov / ms_plain, 4)
         # The vendor library on the same inputs, for reference only: torch's
         # bf16 matmul (hipBLASLt) of the same row-major A and B, contiguous.
         if p.a_rs == w.K and p.b_rs == w.N and p.a_cs == 1 and p.b_cs == 1:

@@ -70,6 +70,16 @@ typedef enum migemm_status {
  * K > 0.  gemm_plan_get_info reports the choice (stream_k_tiles). */
 #define MIGEMM_F_STREAM_K 0x2u
 #define MIGEMM_F_STREAM_K_FORCE 0x4u
+/* With MIGEMM_F_TILE_CONSUMER (else INVALID_ARG): run the consumer stage of
+ * each tile inside the next tile's main loop, fetching the tile back from D,
+ * instead of right after the tile's commit on the tile still staged in LDS.
+ * Same results bit for bit.  The overlap is CUTLASS issue #2900's goal --
+ * consumer work running while the MMA waves start the next tile -- but here
+ * the consumer work shares the MMA waves, and for this consumer stage its
+ * cost inside the K loop is larger than the work itself (about 4% of the
+ * 8192^3 bf16 kernel's time).  It is the form for consumer work that waits
+ * on long transfers rather than computing. */
+#define MIGEMM_F_CONSUMER_OVERLAP 0x8u
 
 /* Output tile of the persistent scheduler (and the hand-off unit). */
 #define MIGEMM_TILE_M 256
@@ -189,8 +199,10 @@ int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* 
 
 /* gemm_run, and in the same kernel a consumer stage fed through a 2-slot
  * tile hand-off ring: every finished 256 x 256 tile of D is committed by the
- * waves that stored it and, while the next tile's main loop runs, consumer
- * work waits for it, reads it back from D, and then releases the slot.  For
+ * waves that stored it; the consumer work waits for the commit, reads the
+ * tile (as staged in LDS by the epilogue, or -- with
+ * MIGEMM_F_CONSUMER_OVERLAP, while the next tile's main loop runs -- back
+ * from D), and then releases the slot.  For
  * the tile at tile column t = n / 256 it writes, for each row r of the tile,
  * over the bf16 values x_j = D[r][256t + j], j = 0 .. 255 (columns at or
  * past N read as +0.0 for the sum and are left out of the maximum):

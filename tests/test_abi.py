@@ -112,6 +112,10 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(flags=migemm.MIGEMM_F_STREAM_K), migemm.MIGEMM_OK),
     (dict(flags=migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_TILE_CONSUMER),
      migemm.MIGEMM_ERR_UNSUPPORTED),                                        # consumer: whole tiles
+    (dict(flags=migemm.MIGEMM_F_CONSUMER_OVERLAP), migemm.MIGEMM_ERR_INVALID_ARG),  # no consumer
+    (dict(flags=migemm.MIGEMM_F_CONSUMER_OVERLAP | migemm.MIGEMM_F_TILE_CONSUMER), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_CONSUMER_OVERLAP | migemm.MIGEMM_F_TILE_CONSUMER |
+          migemm.MIGEMM_F_STREAM_K_FORCE), migemm.MIGEMM_ERR_UNSUPPORTED),
     (dict(max_workgroups=-1), migemm.MIGEMM_ERR_INVALID_ARG),
     (dict(K=5001, a_rs=5008), migemm.MIGEMM_ERR_MISALIGNED),                # K-contiguous A, K%8
 ])
@@ -195,3 +199,12 @@ def test_plan_create_without_a_gpu_reports_device_error():
     with pytest.raises(migemm.MigemmError) as e:
         migemm.gemm_plan_create(desc_for(W, M=-1))
     assert e.value.status == migemm.MIGEMM_ERR_INVALID_ARG
+
+
+def test_header_constants_match_the_binding():
+    # Every #define of the header has the same value in the Python binding.
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"#define (MIGEMM_\w+) (0x[0-9a-fA-F]+|\d+)u?\b", text))
+    assert "MIGEMM_F_CONSUMER_OVERLAP" in defines and len(defines) >= 6
+    for name, value in defines.items():
+        assert getattr(migemm, name) == int(value, 0), name

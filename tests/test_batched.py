@@ -104,16 +104,18 @@ def test_batched_stream_k_ranges_cross_batches():
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
 
 
-def test_batched_tile_consumer():
+@pytest.mark.parametrize("overlap", [False, True], ids=["staged", "overlap"])
+def test_batched_tile_consumer(overlap):
     g = torch.Generator().manual_seed(44)
     L, M, N = 3, 520, 600
     b = Batched(g, L, M, N, 136, "row", "row")
-    plan = migemm.Plan(b.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER, max_workgroups=4))
+    flags = migemm.MIGEMM_F_TILE_CONSUMER | (migemm.MIGEMM_F_CONSUMER_OVERLAP if overlap else 0)
+    plan = migemm.Plan(b.desc(flags=flags, max_workgroups=4))
     ld = (N + 255) // 256
     poison = torch.full((L * M, ld), 0x7FBADBAD, dtype=torch.int32, device="cuda").view(torch.float32)
     rs, rm = poison.clone(), poison.clone()
     D, Dc = b.new_d(), b.new_d()
-    print("[batched] tile consumer", flush=True)
+    print(f"[batched] tile consumer overlap={overlap}", flush=True)
     migemm.gemm_run_with_tile_consumer(plan.handle, b.A, b.B, None, D, b.p0.alpha, 0.0, rs, rm, Dc)
     torch.cuda.synchronize()
     b.check(D)

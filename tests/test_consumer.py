@@ -4,9 +4,13 @@ gemm_run_with_tile_consumer must give the same D as gemm_run, bit for bit;
 its consumer outputs have exactly one correct value given that D: a bit copy
 of D, and per 256-column tile slice of every row an fp32 sum in the fixed
 chunk-then-tree order and the largest non-NaN value (-0 < +0), which the
-oracle recomputes from the GPU's own D and which must match exactly.  Outputs are poisoned first with a NaN whose payload no result can
-carry (results derived from bf16 values have zero low 16 bits), so an
-unconsumed tile shows."""
+oracle recomputes from the GPU's own D and which must match exactly.
+Outputs are poisoned first with a NaN whose payload no result can carry
+(results derived from bf16 values have zero low 16 bits), so an unconsumed
+tile shows.  Both schedules of the consumer stage run every case: right
+after each tile's commit on the tile staged in LDS (the default), and
+inside the next tile's K loop on the tile fetched back from D
+(MIGEMM_F_CONSUMER_OVERLAP); their outputs must agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -24,8 +28,12 @@ def poisoned(rows, cols):
     return torch.full((rows, cols), POISON, dtype=torch.int32, device="cuda").view(torch.float32)
 
 
-def run_consumer(p: Problem, max_workgroups=0):
-    plan = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER, max_workgroups=max_workgroups))
+MODES = {"staged": migemm.MIGEMM_F_TILE_CONSUMER,
+         "overlap": migemm.MIGEMM_F_TILE_CONSUMER | migemm.MIGEMM_F_CONSUMER_OVERLAP}
+
+
+def run_consumer(p: Problem, max_workgroups=0, mode="staged"):
+    plan = migemm.Plan(p.desc(flags=MODES[mode], max_workgroups=max_workgroups))
     ld = (p.N + 255) // 256
     D = p.new_d()
     Dc = p.new_d()
@@ -54,11 +62,12 @@ def check_consumer_outputs(p: Problem, D, Dc, rs, rm):
     assert same_m.all(), "row maxima differ at %s" % (np.argwhere(~same_m)[:5].tolist(),)
 
 
-def test_tile_consumer_workload_8192():
+@pytest.mark.parametrize("mode", MODES)
+def test_tile_consumer_workload_8192(mode):
     w = synth.WORKLOADS[3]
-    print(f"[consumer] workload {w.name}", flush=True)
+    print(f"[consumer] workload {w.name} {mode}", flush=True)
     p = Problem.from_workload(w).to_device()
-    plan, D, Dc, rs, rm = run_consumer(p)
+    plan, D, Dc, rs, rm = run_consumer(p, mode=mode)
     r = check_sampled(p, D, n_random=4096, seed=w.seed)
     assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, r
     check_consumer_outputs(p, D, Dc, rs, rm)
@@ -75,10 +84,12 @@ def test_tile_consumer_workload_8192():
     (1024, 1280, 1000, 3),    # uneven tiles per workgroup
     (768, 768, 8, 2),         # K shorter than the consumer's 33 steps
 ])
-def test_tile_consumer_shapes(M, N, K, mw):
+@pytest.mark.parametrize("mode", MODES)
+def test_tile_consumer_shapes(M, N, K, mw, mode):
     g = torch.Generator().manual_seed(M + N + K + mw)
     p = Problem.random(g, M, N, K, "row", "row", dist="normal", alpha=0.5, beta=0.25).to_device()
-    plan, D, Dc, rs, rm = run_consumer(p, mw)
+    print(f"[consumer] {M}x{N}x{K} grid cap {mw} {mode}", flush=True)
+    plan, D, Dc, rs, rm = run_consumer(p, mw, mode)
     r = check_full(p, D)
     assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, r
     check_consumer_outputs(p, D, Dc, rs, rm)
@@ -114,7 +125,8 @@ def special_rows(rng, n):
     return rows
 
 
-def test_tile_consumer_special_values():
+@pytest.mark.parametrize("mode", MODES)
+def test_tile_consumer_special_values(mode):
     # alpha = -1 and beta = 1 with zero rows in A give D = (-0) + C exactly on
     # those rows, so C plants NaN, +-inf, -0 and subnormal codes in D.  N has
     # a 56-column tail, so both the whole-slice and the partial-slice forms
@@ -129,9 +141,9 @@ def test_tile_consumer_special_values():
     for r in range(0, M, 2):
         A[r, :] = 0
         C[r, :N] = kinds[(r // 2) % len(kinds)]
-    print(f"[consumer] special values {M}x{N}x{K}", flush=True)
+    print(f"[consumer] special values {M}x{N}x{K} {mode}", flush=True)
     p.to_device()
-    plan, D, Dc, rs, rm = run_consumer(p)
+    plan, D, Dc, rs, rm = run_consumer(p, mode=mode)
     check_consumer_outputs(p, D, Dc, rs, rm)
     dc = codes(D).reshape(p.d_shape)[:, :N]
     want = C[0::2, :N]
@@ -145,20 +157,24 @@ def test_tile_consumer_special_values():
     assert torch.equal(D.view(torch.int16), D2.view(torch.int16)), "consumer variant changed D"
 
 
-def test_tile_consumer_other_layouts_and_fp8():
+@pytest.mark.parametrize("mode", MODES)
+def test_tile_consumer_other_layouts_and_fp8(mode):
     g = torch.Generator().manual_seed(77)
     for la, lb, dt in [("col", "col", synth.BF16), ("row", "col", synth.E4M3), ("col", "row", synth.E4M3)]:
         p = Problem.random(g, 520, 700, 256, la, lb, dtype=dt, alpha=0.03125).to_device()
-        plan, D, Dc, rs, rm = run_consumer(p)
+        print(f"[consumer] layouts {la} {lb} {dt} {mode}", flush=True)
+        plan, D, Dc, rs, rm = run_consumer(p, mode=mode)
         r = check_full(p, D)
         assert r["n_fail"] == 0, (la, lb, dt, r)
         check_consumer_outputs(p, D, Dc, rs, rm)
 
 
-def test_tile_consumer_is_deterministic_across_grids():
+def test_tile_consumer_is_deterministic_across_grids_and_schedules():
+    # Same outputs bit for bit whatever the grid and whichever schedule runs
+    # the consumer stage.
     g = torch.Generator().manual_seed(9)
     p = Problem.random(g, 1280, 1024, 264, "row", "row", dist="normal").to_device()
-    outs = [run_consumer(p, mw) for mw in (0, 5, 0)]
+    outs = [run_consumer(p, mw, mode) for mw in (0, 5, 0) for mode in MODES]
     for o in outs[1:]:
         for a, b in zip(o[1:], outs[0][1:]):
             assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),

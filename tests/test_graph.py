@@ -64,10 +64,12 @@ def test_graph_plain_and_stream_k():
     replay_and_check(g, [D1, D2], want, lambda: junk.uniform_())
 
 
-def test_graph_tile_consumer():
+@pytest.mark.parametrize("overlap", [False, True], ids=["staged", "overlap"])
+def test_graph_tile_consumer(overlap):
     gen = torch.Generator().manual_seed(12)
     p = Problem.random(gen, 768, 1000, 264, "row", "row", dist="normal").to_device()
-    plan = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER, max_workgroups=3))
+    flags = migemm.MIGEMM_F_TILE_CONSUMER | (migemm.MIGEMM_F_CONSUMER_OVERLAP if overlap else 0)
+    plan = migemm.Plan(p.desc(flags=flags, max_workgroups=3))
     ld = (p.N + 255) // 256
     D, Dc = p.new_d(), p.new_d()
     rs = torch.empty((p.M, ld), dtype=torch.float32, device="cuda")

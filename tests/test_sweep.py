@@ -1,6 +1,6 @@
 """Seeded sweep (GPU): random valid combinations of shape, operand layouts,
 element type, alpha/beta, D orientation, batch count, grid cap and mode
-(whole tiles, forced stream-K, tile consumer), each checked in full against
+(whole tiles, forced stream-K, tile consumer in either schedule), each checked in full against
 the oracle; the consumer's copy and statistics exactly.  The draws are fixed
 by the seed, so a failure names a reproducible case."""
 import numpy as np
@@ -33,8 +33,9 @@ def draw(i):
     beta = float(rng.choice([0.0, 0.5, -1.0])) if dtype == synth.BF16 else 0.0
     L = int(rng.choice([1, 1, 2, 3]))
     mw = int(rng.choice([0, 0, 1, 3, 7, 13]))
+    overlap = bool(rng.random() < 0.5)   # the consumer's schedule (drawn last: earlier draws kept)
     return dict(dtype=dtype, la=str(la), lb=str(lb), mode=str(mode), d_layout=d_layout, M=M, N=N,
-                K=K, beta=beta, L=L, mw=mw)
+                K=K, beta=beta, L=L, mw=mw, overlap=overlap)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
@@ -58,7 +59,8 @@ def test_sweep(i):
         D2 = run(b, plan, ws)
         assert torch.equal(D1.view(torch.int16), D2.view(torch.int16)), "stream-K runs differ"
     else:
-        plan = migemm.Plan(b.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER, max_workgroups=c["mw"]))
+        flags = migemm.MIGEMM_F_TILE_CONSUMER | (migemm.MIGEMM_F_CONSUMER_OVERLAP if c["overlap"] else 0)
+        plan = migemm.Plan(b.desc(flags=flags, max_workgroups=c["mw"]))
         L, M, N = c["L"], c["M"], c["N"]
         ld = (N + 255) // 256
         poison = torch.full((L * M, ld), 0x7FBADBAD, dtype=torch.int32, device="cuda")

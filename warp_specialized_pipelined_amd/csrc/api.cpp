@@ -78,7 +78,10 @@ int validate(const migemm_desc* d, Canon* out) {
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0)
     return MIGEMM_ERR_INVALID_ARG;
   constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
-  if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | kStreamK)) != 0) return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | kStreamK)) != 0)
+    return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & MIGEMM_F_CONSUMER_OVERLAP) && !(d->flags & MIGEMM_F_TILE_CONSUMER))
+    return MIGEMM_ERR_INVALID_ARG;
   if ((d->flags & MIGEMM_F_TILE_CONSUMER) && (d->flags & kStreamK))
     return MIGEMM_ERR_UNSUPPORTED;  // the consumer works on whole tiles
   const int es = elem_size(d->a_type);
@@ -209,6 +212,7 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   p->sel.a_kmajor = oa.row_major;   // A row-major = K-contiguous
   p->sel.b_kmajor = !ob.row_major;  // B column-major = K-contiguous
   p->sel.consumer = false;
+  p->sel.consumer_overlap = (desc->flags & MIGEMM_F_CONSUMER_OVERLAP) != 0;
 
   KernelArgs& a = p->base;
   a.M = c.M;

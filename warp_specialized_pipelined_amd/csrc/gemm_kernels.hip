@@ -4,7 +4,8 @@
 // hands it, the workgroup runs the pipelined K loop into a 256 x 256 fp32
 // accumulator tile (128 x 128 per wave) and then the epilogue.  Stream-K
 // kernels then take their range of K-stage units of the remaining tiles
-// (streamk.hpp).
+// (streamk.hpp); tile-consumer kernels pass each finished tile through the
+// hand-off ring to the consumer stage (handoff.hpp).
 #include <hip/hip_runtime.h>
 
 #include "kernel/epilogue.hpp"
@@ -31,14 +32,14 @@ struct LaneIds {
   }
 };
 
-template <int ES, bool AK, bool BK, bool CONS, bool SK>
+template <int ES, bool AK, bool BK, int CONS, bool SK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
-  static_assert(!(CONS && SK), "the tile consumer runs on whole tiles only");
+  static_assert(!(CONS != kConsNone && SK), "the tile consumer runs on whole tiles only");
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int first = persistent_slot(blockIdx.x, gridDim.x);
   Accum acc;
-  if constexpr (!CONS) {
+  if constexpr (CONS == kConsNone) {
     NoSideWork none;
     const int whole = SK ? a.sk_first : a.num_tiles;  // tiles taken whole
     for (int L = first; L < whole; L += gridDim.x) {
@@ -52,6 +53,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       barrier();          // ... in every wave before the ring is refilled
     }
     if constexpr (SK) stream_k_tiles<ES, AK, BK>(acc, a, first, gridDim.x, lane, wave);
+  } else if constexpr (CONS == kConsStaged) {
+    // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
+    // Once all four waves have committed it, each wave runs the consumer
+    // stage on its 64 rows of the tile as the epilogue left it staged in
+    // LDS, and releases the slot before the next K loop refills the ring
+    // over the staging area.
+    HandoffRing::init();
+    __syncthreads();
+    TileConsumer cons;
+    cons.idle();
+    NoSideWork none;
+    int n = 0;
+    for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
+      const TileCoord t = tile_of(L, a);
+      const KernelArgs ab = batch_args(a, t.l);
+      const LaneIds id(lane, wave);
+      mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
+      const int s = n % kHandoffSlots;
+      HandoffRing::acquire(s, n / kHandoffSlots);
+      const LaneIds ie(lane, wave);
+      epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
+      HandoffRing::commit(s, L, wave, lane);
+      cons.begin(a, s, n / kHandoffSlots, wave, lane);
+      cons.drain_staged(wave, lane);
+      wait_lgkmcnt<0>();  // staging reads done ...
+      barrier();          // ... in every wave before the ring is refilled
+    }
   } else {
     // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
     // The consumer stage of tile n runs inside tile n+1's K loop; the last
@@ -85,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
 
 typedef void (*kernel_fn)(KernelArgs);
 
-template <int ES, bool CONS, bool SK>
+template <int ES, int CONS, bool SK>
 static kernel_fn pick(bool ak, bool bk) {
   if (ak) return bk ? gemm_kernel<ES, true, true, CONS, SK> : gemm_kernel<ES, true, false, CONS, SK>;
   return bk ? gemm_kernel<ES, false, true, CONS, SK> : gemm_kernel<ES, false, false, CONS, SK>;
@@ -93,9 +121,10 @@ static kernel_fn pick(bool ak, bool bk) {
 
 template <int ES>
 static kernel_fn pick_mode(const KernelSelect& s) {
-  if (s.consumer) return pick<ES, true, false>(s.a_kmajor, s.b_kmajor);
-  if (s.stream_k) return pick<ES, false, true>(s.a_kmajor, s.b_kmajor);
-  return pick<ES, false, false>(s.a_kmajor, s.b_kmajor);
+  if (s.consumer && s.consumer_overlap) return pick<ES, kConsOverlap, false>(s.a_kmajor, s.b_kmajor);
+  if (s.consumer) return pick<ES, kConsStaged, false>(s.a_kmajor, s.b_kmajor);
+  if (s.stream_k) return pick<ES, kConsNone, true>(s.a_kmajor, s.b_kmajor);
+  return pick<ES, kConsNone, false>(s.a_kmajor, s.b_kmajor);
 }
 
 static kernel_fn select(const KernelSelect& s) {

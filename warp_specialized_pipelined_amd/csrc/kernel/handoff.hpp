@@ -21,9 +21,19 @@
 // Every wave is both a producer (its quarter of the tile) and a consumer (64
 // rows of the tile), because on gfx950 all waves of a kernel get the same
 // register allocation and the 256 accumulator registers of a 128 x 128 wave
-// tile leave no room for extra waves.  The consumer work on tile n is spread
-// over the first iterations of tile n+1's K loop, one 16-byte chunk per lane
-// per iteration, so it runs in the shadow of the MFMAs.
+// tile leave no room for extra waves.  The consumer work runs on one of two
+// schedules:
+//   staged (default): right after the tile's commit, on the tile as the
+//     epilogue left it staged in LDS (drain_staged), before the next K loop
+//     refills the ring over the staging area;
+//   overlapped: spread over the first iterations of tile n+1's K loop, one
+//     16-byte chunk per lane per iteration fetched back from D, in the
+//     shadow of the MFMAs (after_barrier and compute<>), the last tile's
+//     after the loop from its staging.
+// The overlap is what the hand-off ring is for when consumer work waits on
+// memory or links; for this consumer stage, whose work is short arithmetic,
+// the staged schedule costs less: the K loop's side work holds the MFMA
+// waves longer than the work takes on its own.
 //
 // Consumer work for a 256 x 256 tile at tile column t: for each of its rows r,
 // over the tile's columns (those past N read as +0.0 for the sum and are left
@@ -149,7 +159,7 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // keeps every wait explicit: the compiler never sees an outstanding load, so
 // it never answers one with a vmcnt(0) that would also drain the ring.
 //
-// Inside the K loop a step takes three iterations:
+// Overlapped schedule -- inside the K loop a step takes three iterations:
 //   iteration i:   fetch (after the barrier, before the stage loads);
 //   iteration i+1: after its barrier -- whose wait covered the fetch -- read
 //                  the landing slot back; fold the 16 bytes in between the
@@ -410,14 +420,15 @@ struct TileConsumer {
     return q * kStagingWaveBytes + (row & 127) * kStagingRowBytes + (col & 127) * 2;
   }
 
-  // The last tile of the workgroup, after its epilogue: the tile is still
-  // staged in LDS (every wave staged its quarter there, and no K loop
-  // follows to overwrite it), so every step is read there instead of being
-  // fetched back from D -- at the kernel's end, when every compute unit
-  // drains at once and the fetches would queue for memory together.  The
-  // bytes are the ones the epilogue stored to D.  The wait in begin() saw
-  // all four waves commit, which orders their staging writes before these
-  // reads.
+  // The whole consumer stage of a tile whose epilogue has just staged it in
+  // LDS (every wave staged its quarter there, and the ring is refilled only
+  // after the caller's next barrier): every step is read there instead of
+  // being fetched back from D.  The bytes are the ones the epilogue stored
+  // to D.  The wait in begin() saw all four waves commit, which orders
+  // their staging writes before these reads.  The staged schedule runs it
+  // for every tile; the overlapped one for the workgroup's last tile, at the
+  // kernel's end, where every compute unit drains at once and fetches would
+  // queue for memory together.
   __device__ __forceinline__ void drain_staged(int wave, int lane) {
     asm volatile("" : "+v"(lane));  // (as in begin)
     while (uni(active)) {

@@ -29,8 +29,9 @@ constexpr int kStagingRowBytes = kWaveTile * 2 + 16;                 // 272
 constexpr int kStagingWaveBytes = kWaveTile * kStagingRowBytes;      // 34816
 constexpr int kStagingBytes = kWaves * kStagingWaveBytes;            // 139264
 constexpr int kPlainLdsBytes = kStagingBytes > kRingBytes ? kStagingBytes : kRingBytes;
-// Consumer-stage landing slots: per wave kConsumerDepth slots of 1 KiB (16
-// bytes per lane), past both the ring and the staging area.  The consumer
+// Consumer-stage landing slots (overlapped consumer): per wave
+// kConsumerDepth slots of 1 KiB (16 bytes per lane), past both the ring and
+// the staging area.  The consumer
 // fetches while the K loop runs (so the slots must not overlap the ring),
 // and one wave may still be draining its consumer work while another
 // already stages its epilogue (so they must not overlap the staging either).
@@ -38,6 +39,10 @@ constexpr int kConsumerDepth = 4;
 constexpr int kConsumerSlotOffset = kPlainLdsBytes;
 constexpr int kConsumerSlotBytes = 64 * 16;
 constexpr int kConsumerEnd = kConsumerSlotOffset + kWaves * kConsumerDepth * kConsumerSlotBytes;
+// How a kernel runs the tile consumer stage: not at all; right after the
+// tile's commit, on the tile as the epilogue staged it in LDS; or inside the
+// next tile's K loop, fetching the tile back from D.
+enum ConsumerMode { kConsNone = 0, kConsStaged = 1, kConsOverlap = 2 };
 // Tile hand-off ring: two slots of {tile id, full count, empty count}.
 constexpr int kHandoffSlots = 2;
 constexpr int kHandoffOffset = kConsumerEnd;

@@ -13,6 +13,7 @@ struct KernelSelect {
   bool a_kmajor;    // A is K-contiguous
   bool b_kmajor;    // B is K-contiguous
   bool consumer;    // tile hand-off + consumer stage
+  bool consumer_overlap;  // the consumer stage inside the next tile's K loop
   bool stream_k;    // stream-K units after the whole tiles (not with consumer)
 };
 

@@ -28,6 +28,7 @@ MIGEMM_ERR_TIMEOUT = -6
 MIGEMM_F_TILE_CONSUMER = 0x1
 MIGEMM_F_STREAM_K = 0x2
 MIGEMM_F_STREAM_K_FORCE = 0x4
+MIGEMM_F_CONSUMER_OVERLAP = 0x8
 MIGEMM_TILE_M = 256
 MIGEMM_TILE_N = 256
 
