@@ -301,72 +301,81 @@ struct TileConsumer {
 
   // The fold, in three parts: the lane's chunk of 8 columns, the tree over
   // the 32 lanes of each row, and the row totals.
+  //
+  // Part 1: the lane's chunk sum (in column order) and maximum key.
+  __device__ __forceinline__ void chunk_fold(const u32x4& x, int lane, float& s_out,
+                                             int32_t& mk_out) const {
+    float s;
+    int32_t mk;
+    if (__builtin_expect(ncols == kTileN, 1)) {
+      // A whole row slice: no column checks; the maximum on both halves
+      // of each word at once.
+      s = bf16_lo(x[0]);
+      s = s + bf16_hi(x[0]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        s = s + bf16_lo(x[w]);
+        s = s + bf16_hi(x[w]);
+      }
+      s16x2 m2 = max_keys2(x[0]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) m2 = __builtin_elementwise_max(m2, max_keys2(x[w]));
+      mk = max((int32_t)m2.x, (int32_t)m2.y);
+    } else {
+      const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
+      s = 0.0f;
+      mk = kNoKey;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
+        const float y = e < n ? __uint_as_float(h << 16) : 0.0f;
+        s = e == 0 ? y : s + y;
+        mk = max(mk, e < n ? max_key(h) : kNoKey);
+      }
+    }
+    s_out = s;
+    mk_out = mk;
+  }
+  // Part 2: adjacent chunks first, a balanced tree over the 32 lanes of a
+  // row.
+  __device__ __forceinline__ static void row_tree(float& s, int32_t& mk) {
+    s += __int_as_float(dpp<kDppXor1>(__float_as_int(s)));
+    mk = max(mk, dpp<kDppXor1>(mk));
+    s += __int_as_float(dpp<kDppXor2>(__float_as_int(s)));
+    mk = max(mk, dpp<kDppXor2>(mk));
+    s += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(s)));
+    mk = max(mk, dpp<kDppHalfMirror>(mk));
+    s += __int_as_float(dpp<kDppMirror>(__float_as_int(s)));
+    mk = max(mk, dpp<kDppMirror>(mk));
+  }
+  // Part 3: the row totals of step j.  Lanes 0-15 and 16-31 hold the two
+  // halves of the first row, lanes 32-47 and 48-63 those of the second.
+  // Row 2j's totals go to lane 2j of the tile's statistics registers, row
+  // 2j+1's to lane 2j+1; they leave with one store after the last step.
+  __device__ __forceinline__ void row_totals(float s, int32_t mk, int j, int lane) {
+    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
+    const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16));
+    const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32));
+    const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48));
+    const int32_t m01 = max(__builtin_amdgcn_readlane(mk, 0), __builtin_amdgcn_readlane(mk, 16));
+    const int32_t m23 = max(__builtin_amdgcn_readlane(mk, 32), __builtin_amdgcn_readlane(mk, 48));
+    const int r = uni(2 * j);
+    const float sa = s0 + s1, sb = s2 + s3;
+    st_sum = lane == r ? sa : (lane == r + 1 ? sb : st_sum);
+    st_max = lane == r ? m01 : (lane == r + 1 ? m23 : st_max);
+  }
+
   template <int P>
   __device__ __forceinline__ void compute(int lane) {
     // Only 32 of a tile's iterations fold a step; the others skip the work
     // (a uniform branch that jumps over VALU code only, never over MFMAs).
     if (!uni(folding)) return;
     if constexpr (P == 0) {
-      float s;
-      int32_t mk;
-      if (__builtin_expect(ncols == kTileN, 1)) {
-        // A whole row slice: no column checks; the maximum on both halves
-        // of each word at once.
-        s = bf16_lo(v[0]);
-        s = s + bf16_hi(v[0]);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          s = s + bf16_lo(v[w]);
-          s = s + bf16_hi(v[w]);
-        }
-        s16x2 m2 = max_keys2(v[0]);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) m2 = __builtin_elementwise_max(m2, max_keys2(v[w]));
-        mk = max((int32_t)m2.x, (int32_t)m2.y);
-      } else {
-        const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
-        s = 0.0f;
-        mk = kNoKey;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
-          const float x = e < n ? __uint_as_float(h << 16) : 0.0f;
-          s = e == 0 ? x : s + x;
-          mk = max(mk, e < n ? max_key(h) : kNoKey);
-        }
-      }
-      sum = s;
-      mkey = mk;
+      chunk_fold(v, lane, sum, mkey);
     } else if constexpr (P == 1) {
-      // Adjacent chunks first: a balanced tree over the 32 lanes of a row.
-      float s = sum;
-      int32_t mk = mkey;
-      s += __int_as_float(dpp<kDppXor1>(__float_as_int(s)));
-      mk = max(mk, dpp<kDppXor1>(mk));
-      s += __int_as_float(dpp<kDppXor2>(__float_as_int(s)));
-      mk = max(mk, dpp<kDppXor2>(mk));
-      s += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(s)));
-      mk = max(mk, dpp<kDppHalfMirror>(mk));
-      s += __int_as_float(dpp<kDppMirror>(__float_as_int(s)));
-      mk = max(mk, dpp<kDppMirror>(mk));
-      sum = s;
-      mkey = mk;
+      row_tree(sum, mkey);
     } else {
-      // Lanes 0-15 and 16-31 hold the two halves of the first row, lanes
-      // 32-47 and 48-63 those of the second.
-      const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 0));
-      const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 16));
-      const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 32));
-      const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), 48));
-      const int32_t m01 = max(__builtin_amdgcn_readlane(mkey, 0), __builtin_amdgcn_readlane(mkey, 16));
-      const int32_t m23 = max(__builtin_amdgcn_readlane(mkey, 32), __builtin_amdgcn_readlane(mkey, 48));
-      // Row 2j's totals go to lane 2j of the tile's statistics registers,
-      // row 2j+1's to lane 2j+1; they leave with one store after the last
-      // step.
-      const int r = uni(2 * fold_j);
-      const float sa = s0 + s1, sb = s2 + s3;
-      st_sum = lane == r ? sa : (lane == r + 1 ? sb : st_sum);
-      st_max = lane == r ? m01 : (lane == r + 1 ? m23 : st_max);
+      row_totals(sum, mkey, fold_j, lane);
       folding = false;
       pending = true;
       pend_j = fold_j;
@@ -375,30 +384,36 @@ struct TileConsumer {
 
   // Store the pending step's copy; after the tile's last step also the row
   // statistics, and release the slot.
-  __device__ __forceinline__ void store_pending(int lane) {
-    if (!uni(pending)) return;
-    pending = false;
-    const int j = uni(pend_j);
+  // The copy of step j (16 bytes per lane).
+  __device__ __forceinline__ void store_copy(const u32x4& x, int j, int lane) const {
     const uint32_t o = at(lane_off, step_bytes, j);
     if (__builtin_expect(ncols == kTileN, 1)) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, cpy, o, 0, kCpolNt);
+      __builtin_amdgcn_raw_buffer_store_b128(x, cpy, o, 0, kCpolNt);
     } else {
       // A tile cut short by N: column by column, past-N ones out of range.
       const int n = ncols - 8 * (lane & 31);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v[e >> 1] >> (16 * (e & 1))), cpy,
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(x[e >> 1] >> (16 * (e & 1))), cpy,
                                               e < n ? o + 2 * e : kOobOffset, 0, 0);
     }
-    if (j == kSteps - 1) {
-      // All 64 rows' statistics at once: 64 lanes, one entry each.
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st_sum), rsum, stat_lane_off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(st_max)), rmax,
-                                            stat_lane_off, 0, 0);
-      active = false;
-      // The tile's reads all completed before their values were folded.
-      HandoffRing::release(slot, lane);
-    }
+  }
+  // After the tile's last step: all 64 rows' statistics at once (64 lanes,
+  // one entry each), and the slot is released -- the tile's reads all
+  // completed before their values were folded.
+  __device__ __forceinline__ void finish_tile(int lane) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st_sum), rsum, stat_lane_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(st_max)), rmax,
+                                          stat_lane_off, 0, 0);
+    active = false;
+    HandoffRing::release(slot, lane);
+  }
+  __device__ __forceinline__ void store_pending(int lane) {
+    if (!uni(pending)) return;
+    pending = false;
+    const int j = uni(pend_j);
+    store_copy(v, j, lane);
+    if (j == kSteps - 1) finish_tile(lane);
   }
 
   // K-loop hook, right after the barrier.
@@ -429,15 +444,33 @@ struct TileConsumer {
   // for every tile; the overlapped one for the workgroup's last tile, at the
   // kernel's end, where every compute unit drains at once and fetches would
   // queue for memory together.
+  //
+  // kStagedBatch steps at a time: their folds are independent chains (LDS
+  // read, chunk sums, butterfly, readlanes), which the compiler interleaves
+  // instead of waiting out each one's latencies in turn.
+  static constexpr int kStagedBatch = 4;
   __device__ __forceinline__ void drain_staged(int wave, int lane) {
+    static_assert(kSteps % kStagedBatch == 0, "whole batches of steps");
     asm volatile("" : "+v"(lane));  // (as in begin)
-    while (uni(active)) {
-      read_back_lane(staged_at(wave, lane, uni(folded)));
-      compute<0>(lane);
-      compute<1>(lane);
-      compute<2>(lane);
-      store_pending(lane);
+    if (!uni(active)) return;
+    for (int j0 = 0; j0 < kSteps; j0 += kStagedBatch) {
+      u32x4 x[kStagedBatch];
+      float s[kStagedBatch];
+      int32_t mk[kStagedBatch];
+#pragma unroll
+      for (int q = 0; q < kStagedBatch; ++q)
+        x[q] = *(const MIGEMM_LDS u32x4*)lds_at(staged_at(wave, lane, j0 + q));
+#pragma unroll
+      for (int q = 0; q < kStagedBatch; ++q) chunk_fold(x[q], lane, s[q], mk[q]);
+#pragma unroll
+      for (int q = 0; q < kStagedBatch; ++q) row_tree(s[q], mk[q]);
+#pragma unroll
+      for (int q = 0; q < kStagedBatch; ++q) row_totals(s[q], mk[q], j0 + q, lane);
+#pragma unroll
+      for (int q = 0; q < kStagedBatch; ++q) store_copy(x[q], j0 + q, lane);
     }
+    fetched = folded = kSteps;
+    finish_tile(lane);
   }
 
   // After the K loop: the steps the loop did not finish.  The ring and this
