@@ -305,6 +305,12 @@ struct TileConsumer {
   // Part 1: the lane's chunk sum (in column order) and maximum key.
   __device__ __forceinline__ void chunk_fold(const u32x4& x, int lane, float& s_out,
                                              int32_t& mk_out) const {
+    chunk_fold_n(x, ncols - 8 * (lane & 31), s_out, mk_out);
+  }
+  // Same for a chunk with n valid columns from its first (n >= 8 whenever
+  // the tile is whole).
+  __device__ __forceinline__ void chunk_fold_n(const u32x4& x, int n, float& s_out,
+                                               int32_t& mk_out) const {
     float s;
     int32_t mk;
     if (__builtin_expect(ncols == kTileN, 1)) {
@@ -322,7 +328,6 @@ struct TileConsumer {
       for (int w = 1; w < 4; ++w) m2 = __builtin_elementwise_max(m2, max_keys2(x[w]));
       mk = max((int32_t)m2.x, (int32_t)m2.y);
     } else {
-      const int n = ncols - 8 * (lane & 31);  // valid columns from this lane's first one
       s = 0.0f;
       mk = kNoKey;
 #pragma unroll
@@ -445,29 +450,47 @@ struct TileConsumer {
   // kernel's end, where every compute unit drains at once and fetches would
   // queue for memory together.
   //
-  // kStagedBatch steps at a time: their folds are independent chains (LDS
-  // read, chunk sums, butterfly, readlanes), which the compiler interleaves
-  // instead of waiting out each one's latencies in turn.
-  static constexpr int kStagedBatch = 4;
+  // With the whole tile in LDS no lane needs another's chunks: lane L folds
+  // row 64 w + L on its own -- its 32 chunk sums, then the same balanced
+  // tree over them in registers -- so the butterfly and the readlanes of
+  // the step-wise fold drop out.  The 32 lanes of 16 rows read one chunk
+  // each at a 272-byte pitch: every bank once, no conflict.  The copy keeps
+  // the step layout (two whole rows per store instruction), kCopyBatch steps
+  // in flight at a time.
+  static constexpr int kCopyBatch = 8;
   __device__ __forceinline__ void drain_staged(int wave, int lane) {
-    static_assert(kSteps % kStagedBatch == 0, "whole batches of steps");
+    static_assert(kSteps % kCopyBatch == 0, "whole batches of steps");
     asm volatile("" : "+v"(lane));  // (as in begin)
     if (!uni(active)) return;
-    for (int j0 = 0; j0 < kSteps; j0 += kStagedBatch) {
-      u32x4 x[kStagedBatch];
-      float s[kStagedBatch];
-      int32_t mk[kStagedBatch];
+    {
+      const int row = wave * 64 + lane;
+      const uint32_t base = 2 * (row >> 7) * kStagingWaveBytes + (row & 127) * kStagingRowBytes;
+      constexpr int kChunks = kTileN / 8;
+      float c[kChunks];
+      int32_t mk = kNoKey;
 #pragma unroll
-      for (int q = 0; q < kStagedBatch; ++q)
+      for (int k = 0; k < kChunks; ++k) {
+        const u32x4 x = *(const MIGEMM_LDS u32x4*)lds_at(
+            base + (k / (kChunks / 2)) * kStagingWaveBytes + (k % (kChunks / 2)) * 16);
+        int32_t m;
+        chunk_fold_n(x, ncols - 8 * k, c[k], m);
+        mk = max(mk, m);
+      }
+      // Adjacent chunks first, as in row_tree.
+#pragma unroll
+      for (int w = 1; w < kChunks; w *= 2)
+#pragma unroll
+        for (int k = 0; k < kChunks; k += 2 * w) c[k] = c[k] + c[k + w];
+      st_sum = c[0];
+      st_max = mk;
+    }
+    for (int j0 = 0; j0 < kSteps; j0 += kCopyBatch) {
+      u32x4 x[kCopyBatch];
+#pragma unroll
+      for (int q = 0; q < kCopyBatch; ++q)
         x[q] = *(const MIGEMM_LDS u32x4*)lds_at(staged_at(wave, lane, j0 + q));
 #pragma unroll
-      for (int q = 0; q < kStagedBatch; ++q) chunk_fold(x[q], lane, s[q], mk[q]);
-#pragma unroll
-      for (int q = 0; q < kStagedBatch; ++q) row_tree(s[q], mk[q]);
-#pragma unroll
-      for (int q = 0; q < kStagedBatch; ++q) row_totals(s[q], mk[q], j0 + q, lane);
-#pragma unroll
-      for (int q = 0; q < kStagedBatch; ++q) store_copy(x[q], j0 + q, lane);
+      for (int q = 0; q < kCopyBatch; ++q) store_copy(x[q], j0 + q, lane);
     }
     fetched = folded = kSteps;
     finish_tile(lane);
