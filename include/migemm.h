@@ -17,7 +17,8 @@
  * producer acquire/commit and consumer wait/release protocol that CUTLASS
  * issue #2900 ("How to build a pipeline between epilogue and communication
  * warp groups?") asks for, so that a consumer stage can work on each finished
- * output tile while the next tile's main loop runs.
+ * output tile; with MIGEMM_F_CONSUMER_OVERLAP it does so while the next
+ * tile's main loop runs.
  *
  * Conventions shared by every entry point:
  *   - all sizes and strides are int64_t; strides are in ELEMENTS;

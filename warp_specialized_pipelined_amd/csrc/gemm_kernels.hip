@@ -81,9 +81,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       barrier();          // ... in every wave before the ring is refilled
     }
   } else {
-    // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
-    // The consumer stage of tile n runs inside tile n+1's K loop; the last
-    // tile's runs after the loop, on the tile as its epilogue staged it.
+    // Overlapped schedule.  Tile n of this workgroup goes through hand-off
+    // slot n % S (use n / S).  The consumer stage of tile n runs inside tile
+    // n+1's K loop; the last tile's runs after the loop, on the tile as its
+    // epilogue staged it.
     HandoffRing::init();
     __syncthreads();
     TileConsumer cons;
