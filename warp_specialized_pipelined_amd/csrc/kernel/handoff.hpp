@@ -43,7 +43,9 @@
 //                   first (c_0 + c_1, c_2 + c_3, ...; then pairs of those, ...)
 //   row_max[r][t] = the largest non-NaN value, with -0 < +0; -inf if none,
 // and the row is copied bit for bit to D_copy.  (The pages leave the
-// consumer's arithmetic open; this order lets 32 lanes share a row.)
+// consumer's arithmetic open; this order lets 32 lanes share a row, as the
+// overlapped schedule does, and gives the same bits when one lane folds the
+// whole row, as the staged schedule does.)
 #pragma once
 
 #include "gfx950.hpp"
