@@ -52,7 +52,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       wait_lgkmcnt<0>();  // staging reads done ...
       barrier();          // ... in every wave before the ring is refilled
     }
-    if constexpr (SK) stream_k_tiles<ES, AK, BK>(acc, a, first, gridDim.x, lane, wave);
+    if constexpr (SK) {
+      // When every tile is split (no whole-tile rounds before), the slot is
+      // the dispatch index itself.  The hardware deals consecutive
+      // workgroups round-robin over the XCDs, so the contributors of one
+      // tile land on different XCDs, and each XCD runs the same K range of
+      // many tiles that share operand panels in its L2 (the remap would give
+      // an XCD all K ranges of a few tiles instead).  Which workgroup holds
+      // which slot does not change the result: the fixup adds the partials
+      // in the order of their K ranges.
+      const int w = a.sk_first == 0 ? (int)blockIdx.x : first;
+      stream_k_tiles<ES, AK, BK>(acc, a, w, gridDim.x, lane, wave);
+    }
   } else if constexpr (CONS == kConsStaged) {
     // Tile n of this workgroup goes through hand-off slot n % S (use n / S).
     // Once all four waves have committed it, each wave runs the consumer
