@@ -71,15 +71,15 @@ typedef enum migemm_status {
  * K > 0.  gemm_plan_get_info reports the choice (stream_k_tiles). */
 #define MIGEMM_F_STREAM_K 0x2u
 #define MIGEMM_F_STREAM_K_FORCE 0x4u
-/* With MIGEMM_F_TILE_CONSUMER (else INVALID_ARG): run the consumer stage of
- * each tile inside the next tile's main loop, fetching the tile back from D,
- * instead of right after the tile's commit on the tile still staged in LDS.
- * Same results bit for bit.  The overlap is CUTLASS issue #2900's goal --
- * consumer work running while the MMA waves start the next tile -- but here
- * the consumer work shares the MMA waves, and for this consumer stage its
- * cost inside the K loop is larger than the work itself (about 4% of the
- * 8192^3 bf16 kernel's time).  It is the form for consumer work that waits
- * on long transfers rather than computing. */
+/* With MIGEMM_F_TILE_CONSUMER (else INVALID_ARG): copy each tile to D_copy
+ * inside the next tile's main loop, fetching it back from D, instead of right
+ * after the tile's commit from the tile still staged in LDS (the row
+ * statistics are folded right after the commit either way).  Same results
+ * bit for bit.  The overlap is CUTLASS issue #2900's goal -- consumer work
+ * running while the MMA waves start the next tile -- but here the consumer
+ * work shares the MMA waves, and in the K loop it costs more than it does
+ * on its own (about 2.5% of the 8192^3 bf16 kernel's time).  It is the form
+ * for consumer work that waits on long transfers rather than computing. */
 #define MIGEMM_F_CONSUMER_OVERLAP 0x8u
 
 /* Output tile of the persistent scheduler (and the hand-off unit). */

@@ -87,15 +87,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
       HandoffRing::commit(s, L, wave, lane);
       cons.begin(a, s, n / kHandoffSlots, wave, lane);
-      cons.drain_staged(wave, lane);
+      cons.fold_staged(wave, lane);
+      cons.copy_staged(wave, lane);
       wait_lgkmcnt<0>();  // staging reads done ...
       barrier();          // ... in every wave before the ring is refilled
     }
   } else {
     // Overlapped schedule.  Tile n of this workgroup goes through hand-off
-    // slot n % S (use n / S).  The consumer stage of tile n runs inside tile
-    // n+1's K loop; the last tile's runs after the loop, on the tile as its
-    // epilogue staged it.
+    // slot n % S (use n / S).  Its row statistics are folded right after its
+    // commit, from the staged tile; its copy runs inside tile n+1's K loop,
+    // fetching the tile back from D (the last tile's from its staging, after
+    // the loop).
     HandoffRing::init();
     __syncthreads();
     TileConsumer cons;
@@ -104,7 +106,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
       const TileCoord t = tile_of(L, a);
       const KernelArgs ab = batch_args(a, t.l);
-      if (n > 0) cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, cons);
       cons.drain(a, wave, lane);
@@ -113,13 +114,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       const LaneIds ie(lane, wave);
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
       HandoffRing::commit(s, L, wave, lane);
+      cons.begin(a, s, n / kHandoffSlots, wave, lane);
+      cons.fold_staged(wave, lane);
       wait_lgkmcnt<0>();
       barrier();
     }
-    if (n > 0) {
-      cons.begin(a, (n - 1) % kHandoffSlots, (n - 1) / kHandoffSlots, wave, lane);
-      cons.drain_staged(wave, lane);
-    }
+    cons.copy_staged(wave, lane);  // the last tile (no-op without tiles)
   }
 }
 

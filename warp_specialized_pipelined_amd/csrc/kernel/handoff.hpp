@@ -21,19 +21,17 @@
 // Every wave is both a producer (its quarter of the tile) and a consumer (64
 // rows of the tile), because on gfx950 all waves of a kernel get the same
 // register allocation and the 256 accumulator registers of a 128 x 128 wave
-// tile leave no room for extra waves.  The consumer work runs on one of two
-// schedules:
-//   staged (default): right after the tile's commit, on the tile as the
-//     epilogue left it staged in LDS (drain_staged), before the next K loop
-//     refills the ring over the staging area;
-//   overlapped: spread over the first iterations of tile n+1's K loop, one
-//     16-byte chunk per lane per iteration fetched back from D, in the
-//     shadow of the MFMAs (after_barrier and compute<>), the last tile's
-//     after the loop from its staging.
+// tile leave no room for extra waves.  Right after the tile's commit each
+// wave folds the row statistics from the tile as the epilogue left it
+// staged in LDS (fold_staged), before the next K loop refills the ring over
+// the staging area.  The copy runs on one of two schedules:
+//   staged (default): at once, from the staged tile (copy_staged);
+//   overlapped: inside tile n+1's K loop, one step per iteration fetched
+//     back from D (after_barrier, drain); the last tile's from its staging.
 // The overlap is what the hand-off ring is for when consumer work waits on
-// memory or links; for this consumer stage, whose work is short arithmetic,
-// the staged schedule costs less: the K loop's side work holds the MFMA
-// waves longer than the work takes on its own.
+// memory or links; for this consumer stage the staged schedule costs less:
+// the K loop's side work holds the MFMA waves longer than the work takes on
+// its own.
 //
 // Consumer work for a 256 x 256 tile at tile column t: for each of its rows r,
 // over the tile's columns (those past N read as +0.0 for the sum and are left
@@ -130,19 +128,6 @@ __device__ __forceinline__ float max_key_value(int32_t key) {
   return __uint_as_float((k ^ ((0u - (k >> 15)) & 0x7FFFu)) << 16);
 }
 
-// Butterfly partner values within groups of 32 lanes (DPP): pairs at
-// distance 1 and 2 (quad permutes), then the mirror images within 8 and 16
-// lanes -- after the earlier levels every lane of a group holds its group's
-// value, so mirroring pairs the same groups as a distance-4 or -8 exchange.
-template <int CTRL>
-__device__ __forceinline__ int32_t dpp(int32_t v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror
-constexpr int kDppMirror = 0x140;     // row_mirror
-
 // The value of lane 0 as a wave-uniform one.  The consumer's counters and
 // flags are the same in every lane; saying so keeps them in SGPRs and their
 // branches scalar (the compiler cannot prove it through the hand-off ring's
@@ -150,32 +135,34 @@ constexpr int kDppMirror = 0x140;     // row_mirror
 // EXEC-masked branches).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// One wave's share of the consumer work on one tile: rows 64w .. 64w+63, two
-// per step.  Step j covers rows 64w + 2j (lanes 0-31) and 64w + 2j + 1 (lanes
-// 32-63); lane l takes the 16 bytes (8 columns) 8 (l % 32) .. + 7 of its row,
-// so every step reads and writes two whole 512-byte rows: the memory
-// pipeline sees 2 long segments per instruction instead of 64 short ones.
+// One wave's share of the consumer work on one tile: rows 64w .. 64w+63.
 //
-// A step's 16 bytes are fetched with an LDS-DMA load into the lane's slot of
-// one of its wave's landing slots.  Going through LDS (like the K-loop ring)
-// keeps every wait explicit: the compiler never sees an outstanding load, so
-// it never answers one with a vmcnt(0) that would also drain the ring.
+// The row statistics are folded right after the tile's commit, from the
+// tile as the epilogue left it staged in LDS, one row per lane: lane L folds
+// row 64 w + L alone -- its 32 chunk sums, then the balanced tree over them
+// in registers.  The 16 rows that one read touches at the staging area's
+// 272-byte pitch hit every bank once.  The statistics leave with one store
+// per array (64 lanes, one entry each).
 //
-// Overlapped schedule -- inside the K loop a step takes three iterations:
-//   iteration i:   fetch (after the barrier, before the stage loads);
+// The copy goes by steps of two rows: step j covers rows 64w + 2j (lanes
+// 0-31) and 64w + 2j + 1 (lanes 32-63); lane l takes the 16 bytes (8
+// columns) 8 (l % 32) .. + 7 of its row, so every store writes two whole
+// 512-byte rows -- the memory pipeline sees 2 long segments per instruction
+// instead of 64 short ones.  The staged schedule copies all 32 steps at
+// once from the staged tile.  The overlapped one copies inside the next
+// tile's K loop, one step per iteration, fetching the tile back from D:
+//   iteration i:   fetch step j with an LDS-DMA load into one of the wave's
+//                  landing slots (after the barrier, before the stage loads);
 //   iteration i+1: after its barrier -- whose wait covered the fetch -- read
-//                  the landing slot back; fold the 16 bytes in between the
-//                  MFMAs that follow (compute<0..2>);
+//                  the landing slot back;
 //   iteration i+2: after its barrier, store the copy.
-// The folds put each row's totals into a lane of two registers (lane L for
-// row 64 w + L), which leave with one store each after the tile's last step:
-// 64 scattered 4-byte entries per instruction instead of 2 per instruction
-// in 64 instructions, which kept the address path busy for hundreds of
-// cycles per step and held up the stage loads behind them.  After the K loop
-// the rest is finished synchronously (drain): every remaining step is
-// fetched at once into the wave's epilogue staging area, which is idle until
-// the wave's own epilogue, so the drain waits for memory once instead of
-// once per few steps.
+// Going through LDS keeps every wait explicit: the compiler never sees an
+// outstanding load, so it never answers one with a vmcnt(0) that would also
+// drain the ring.  Steps the K loop did not reach are finished after it
+// (drain): the ring and the wave's staging area are idle until the wave's
+// epilogue, so the remaining fetches all go out at once into the staging
+// area and the drain waits for memory once.  The workgroup's last tile has
+// no K loop after it and is copied from its staging area.
 struct TileConsumer {
   static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
   // Buffer resources from the tile's origin: D (fetch) and D_copy (store)
@@ -189,25 +176,16 @@ struct TileConsumer {
   int row0;                     // this lane's row within the tile in step 0
   int rows;                     // valid rows of the tile
   int ncols;                    // valid columns of the tile
-  int fetched;                  // steps fetched so far
-  int folded;                   // steps read back (and folded) so far
+  int fetched;                  // copy steps fetched so far
+  int read;                     // copy steps read back so far
   int slot;
-  bool active;                  // steps of this tile remain to be stored
-  // The step being folded in this iteration (folding), and the one whose
-  // results wait for their stores (pending).
-  bool folding, pending;
-  int fold_j, pend_j;
-  u32x4 v;                      // the step's 16 bytes (folding), then its copy (pending)
-  float sum;                    // this lane's chunk sum, then its row half's sum
-  int32_t mkey;                 // same for the maximum, as a key (max_key)
-  // The tile's row statistics, lane L holding row 64 w + L's (filled by the
-  // folds, stored after the last step).
-  float st_sum;
-  int32_t st_max;
+  bool active;                  // copy steps of this tile remain to be stored
+  bool pending;                 // step pend_j is read back and waits for its store
+  int pend_j;
+  u32x4 v;                      // the pending step's 16 bytes
 
   __device__ __forceinline__ void idle() {
     active = false;
-    folding = false;
     pending = false;
   }
 
@@ -264,9 +242,8 @@ struct TileConsumer {
     asm volatile("" : "+v"(lane_off), "+v"(stat_lane_off));
     asm volatile("" : "+s"(step_bytes));
     fetched = 0;
-    folded = 0;
+    read = 0;
     active = true;
-    folding = false;
     pending = false;
   }
 
@@ -278,41 +255,20 @@ struct TileConsumer {
     return ok ? base + (uint32_t)j * step : kOobOffset;
   }
 
-  __device__ __forceinline__ void fetch(int wave) {
-    const int j = uni(fetched);
-    fetched = j + 1;
-    dma16_w5_nt(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
+  // Where the epilogue left this lane's 16 bytes of copy step j: wave q
+  // staged the quarter of rows 128 (q / 2) .. + 127 and columns 128 (q % 2)
+  // .. + 127, row by row at kStagingRowBytes.
+  __device__ __forceinline__ static uint32_t staged_at(int wave, int lane, int j) {
+    const int row = wave * 64 + 2 * j + (lane >> 5);
+    const int col = 8 * (lane & 31);
+    const int q = 2 * (row >> 7) + (col >> 7);
+    return q * kStagingWaveBytes + (row & 127) * kStagingRowBytes + (col & 127) * 2;
   }
 
-  // Read step `folded` back from LDS at `slot` (its fetch must have
-  // completed).
-  __device__ __forceinline__ void read_back_at(uint32_t slot, int lane) {
-    read_back_lane(slot + 16 * lane);
-  }
-  // Same, from this lane's own LDS address.
-  __device__ __forceinline__ void read_back_lane(uint32_t at) {
-    compiler_fence();
-    fold_j = uni(folded);
-    folded = fold_j + 1;
-    v = *(const MIGEMM_LDS u32x4*)lds_at(at);
-    folding = true;
-  }
-  __device__ __forceinline__ void read_back(int wave, int lane) {
-    read_back_at(landing(wave, uni(folded)), lane);
-  }
-
-  // The fold, in three parts: the lane's chunk of 8 columns, the tree over
-  // the 32 lanes of each row, and the row totals.
-  //
-  // Part 1: the lane's chunk sum (in column order) and maximum key.
-  __device__ __forceinline__ void chunk_fold(const u32x4& x, int lane, float& s_out,
+  // The sum (in column order) and maximum key of a chunk of 8 columns with
+  // n valid columns from its first (n >= 8 whenever the tile is whole).
+  __device__ __forceinline__ void chunk_fold(const u32x4& x, int n, float& s_out,
                                              int32_t& mk_out) const {
-    chunk_fold_n(x, ncols - 8 * (lane & 31), s_out, mk_out);
-  }
-  // Same for a chunk with n valid columns from its first (n >= 8 whenever
-  // the tile is whole).
-  __device__ __forceinline__ void chunk_fold_n(const u32x4& x, int n, float& s_out,
-                                               int32_t& mk_out) const {
     float s;
     int32_t mk;
     if (__builtin_expect(ncols == kTileN, 1)) {
@@ -343,54 +299,36 @@ struct TileConsumer {
     s_out = s;
     mk_out = mk;
   }
-  // Part 2: adjacent chunks first, a balanced tree over the 32 lanes of a
-  // row.
-  __device__ __forceinline__ static void row_tree(float& s, int32_t& mk) {
-    s += __int_as_float(dpp<kDppXor1>(__float_as_int(s)));
-    mk = max(mk, dpp<kDppXor1>(mk));
-    s += __int_as_float(dpp<kDppXor2>(__float_as_int(s)));
-    mk = max(mk, dpp<kDppXor2>(mk));
-    s += __int_as_float(dpp<kDppHalfMirror>(__float_as_int(s)));
-    mk = max(mk, dpp<kDppHalfMirror>(mk));
-    s += __int_as_float(dpp<kDppMirror>(__float_as_int(s)));
-    mk = max(mk, dpp<kDppMirror>(mk));
-  }
-  // Part 3: the row totals of step j.  Lanes 0-15 and 16-31 hold the two
-  // halves of the first row, lanes 32-47 and 48-63 those of the second.
-  // Row 2j's totals go to lane 2j of the tile's statistics registers, row
-  // 2j+1's to lane 2j+1; they leave with one store after the last step.
-  __device__ __forceinline__ void row_totals(float s, int32_t mk, int j, int lane) {
-    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
-    const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16));
-    const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 32));
-    const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 48));
-    const int32_t m01 = max(__builtin_amdgcn_readlane(mk, 0), __builtin_amdgcn_readlane(mk, 16));
-    const int32_t m23 = max(__builtin_amdgcn_readlane(mk, 32), __builtin_amdgcn_readlane(mk, 48));
-    const int r = uni(2 * j);
-    const float sa = s0 + s1, sb = s2 + s3;
-    st_sum = lane == r ? sa : (lane == r + 1 ? sb : st_sum);
-    st_max = lane == r ? m01 : (lane == r + 1 ? m23 : st_max);
-  }
 
-  template <int P>
-  __device__ __forceinline__ void compute(int lane) {
-    // Only 32 of a tile's iterations fold a step; the others skip the work
-    // (a uniform branch that jumps over VALU code only, never over MFMAs).
-    if (!uni(folding)) return;
-    if constexpr (P == 0) {
-      chunk_fold(v, lane, sum, mkey);
-    } else if constexpr (P == 1) {
-      row_tree(sum, mkey);
-    } else {
-      row_totals(sum, mkey, fold_j, lane);
-      folding = false;
-      pending = true;
-      pend_j = fold_j;
+  // The row statistics of the tile the epilogue has just staged (every wave
+  // staged its quarter, and the ring is refilled only after the caller's
+  // next barrier; the wait in begin() saw all four waves commit, which
+  // orders their staging writes before these reads).
+  __device__ __forceinline__ void fold_staged(int wave, int lane) {
+    asm volatile("" : "+v"(lane));  // (as in begin)
+    const int row = wave * 64 + lane;
+    const uint32_t base = 2 * (row >> 7) * kStagingWaveBytes + (row & 127) * kStagingRowBytes;
+    constexpr int kChunks = kTileN / 8;
+    float c[kChunks];
+    int32_t mk = kNoKey;
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const u32x4 x = *(const MIGEMM_LDS u32x4*)lds_at(
+          base + (k / (kChunks / 2)) * kStagingWaveBytes + (k % (kChunks / 2)) * 16);
+      int32_t m;
+      chunk_fold(x, ncols - 8 * k, c[k], m);
+      mk = max(mk, m);
     }
+    // The balanced tree, adjacent chunks first.
+#pragma unroll
+    for (int w = 1; w < kChunks; w *= 2)
+#pragma unroll
+      for (int k = 0; k < kChunks; k += 2 * w) c[k] = c[k] + c[k + w];
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0]), rsum, stat_lane_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(mk)), rmax,
+                                          stat_lane_off, 0, 0);
   }
 
-  // Store the pending step's copy; after the tile's last step also the row
-  // statistics, and release the slot.
   // The copy of step j (16 bytes per lane).
   __device__ __forceinline__ void store_copy(const u32x4& x, int j, int lane) const {
     const uint32_t o = at(lane_off, step_bytes, j);
@@ -405,87 +343,21 @@ struct TileConsumer {
                                               e < n ? o + 2 * e : kOobOffset, 0, 0);
     }
   }
-  // After the tile's last step: all 64 rows' statistics at once (64 lanes,
-  // one entry each), and the slot is released -- the tile's reads all
-  // completed before their values were folded.
-  __device__ __forceinline__ void finish_tile(int lane) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st_sum), rsum, stat_lane_off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(st_max)), rmax,
-                                          stat_lane_off, 0, 0);
+
+  // The tile's last copy step is stored: the slot is free again.  The
+  // tile's reads all completed before their values were stored.
+  __device__ __forceinline__ void done(int lane) {
     active = false;
     HandoffRing::release(slot, lane);
   }
-  __device__ __forceinline__ void store_pending(int lane) {
-    if (!uni(pending)) return;
-    pending = false;
-    const int j = uni(pend_j);
-    store_copy(v, j, lane);
-    if (j == kSteps - 1) finish_tile(lane);
-  }
 
-  // K-loop hook, right after the barrier.
-  __device__ __forceinline__ void after_barrier(const KernelArgs& a, int wave, int lane) {
-    (void)a;
-    store_pending(lane);
-    if (!uni(active)) return;
-    if (uni(fetched) > uni(folded)) read_back(wave, lane);
-    if (uni(fetched) < kSteps) fetch(wave);
-  }
-
-  // Where the epilogue left this lane's 16 bytes of step j: wave q staged
-  // the quarter of rows 128 (q / 2) .. + 127 and columns 128 (q % 2) .. +
-  // 127, row by row at kStagingRowBytes.
-  __device__ __forceinline__ static uint32_t staged_at(int wave, int lane, int j) {
-    const int row = wave * 64 + 2 * j + (lane >> 5);
-    const int col = 8 * (lane & 31);
-    const int q = 2 * (row >> 7) + (col >> 7);
-    return q * kStagingWaveBytes + (row & 127) * kStagingRowBytes + (col & 127) * 2;
-  }
-
-  // The whole consumer stage of a tile whose epilogue has just staged it in
-  // LDS (every wave staged its quarter there, and the ring is refilled only
-  // after the caller's next barrier): every step is read there instead of
-  // being fetched back from D.  The bytes are the ones the epilogue stored
-  // to D.  The wait in begin() saw all four waves commit, which orders
-  // their staging writes before these reads.  The staged schedule runs it
-  // for every tile; the overlapped one for the workgroup's last tile, at the
-  // kernel's end, where every compute unit drains at once and fetches would
-  // queue for memory together.
-  //
-  // With the whole tile in LDS no lane needs another's chunks: lane L folds
-  // row 64 w + L on its own -- its 32 chunk sums, then the same balanced
-  // tree over them in registers -- so the butterfly and the readlanes of
-  // the step-wise fold drop out.  The 32 lanes of 16 rows read one chunk
-  // each at a 272-byte pitch: every bank once, no conflict.  The copy keeps
-  // the step layout (two whole rows per store instruction), kCopyBatch steps
-  // in flight at a time.
+  // Staged schedule: the copy steps kCopyBatch at a time from the staged
+  // tile, then the release.
   static constexpr int kCopyBatch = 8;
-  __device__ __forceinline__ void drain_staged(int wave, int lane) {
+  __device__ __forceinline__ void copy_staged(int wave, int lane) {
     static_assert(kSteps % kCopyBatch == 0, "whole batches of steps");
     asm volatile("" : "+v"(lane));  // (as in begin)
     if (!uni(active)) return;
-    {
-      const int row = wave * 64 + lane;
-      const uint32_t base = 2 * (row >> 7) * kStagingWaveBytes + (row & 127) * kStagingRowBytes;
-      constexpr int kChunks = kTileN / 8;
-      float c[kChunks];
-      int32_t mk = kNoKey;
-#pragma unroll
-      for (int k = 0; k < kChunks; ++k) {
-        const u32x4 x = *(const MIGEMM_LDS u32x4*)lds_at(
-            base + (k / (kChunks / 2)) * kStagingWaveBytes + (k % (kChunks / 2)) * 16);
-        int32_t m;
-        chunk_fold_n(x, ncols - 8 * k, c[k], m);
-        mk = max(mk, m);
-      }
-      // Adjacent chunks first, as in row_tree.
-#pragma unroll
-      for (int w = 1; w < kChunks; w *= 2)
-#pragma unroll
-        for (int k = 0; k < kChunks; k += 2 * w) c[k] = c[k] + c[k + w];
-      st_sum = c[0];
-      st_max = mk;
-    }
     for (int j0 = 0; j0 < kSteps; j0 += kCopyBatch) {
       u32x4 x[kCopyBatch];
 #pragma unroll
@@ -494,24 +366,50 @@ struct TileConsumer {
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) store_copy(x[q], j0 + q, lane);
     }
-    fetched = folded = kSteps;
-    finish_tile(lane);
+    fetched = read = kSteps;
+    done(lane);
   }
 
-  // After the K loop: the steps the loop did not finish.  The ring and this
-  // wave's staging area are idle until this wave's epilogue (every wave
-  // passed the loop's closing barrier; the staging area is the wave's own),
-  // so all remaining fetches go out at once, into the staging area, and the
-  // drain waits for memory once.  A step fetched by the loop but not yet
-  // read back is still in its landing slot.
+  // Overlapped schedule.
+  __device__ __forceinline__ void fetch(int wave) {
+    const int j = uni(fetched);
+    fetched = j + 1;
+    dma16_w5_nt(src, lds_at(landing(wave, j)), at(lane_off, step_bytes, j));
+  }
+  // Read step `read` back from LDS at `slot` (its fetch must have completed).
+  __device__ __forceinline__ void read_back_at(uint32_t slot_at, int lane) {
+    compiler_fence();
+    pend_j = uni(read);
+    read = pend_j + 1;
+    v = *(const MIGEMM_LDS u32x4*)lds_at(slot_at + 16 * lane);
+    pending = true;
+  }
+  // Store the pending step's copy; after the tile's last step, release.
+  __device__ __forceinline__ void store_pending(int lane) {
+    if (!uni(pending)) return;
+    pending = false;
+    const int j = uni(pend_j);
+    store_copy(v, j, lane);
+    if (j == kSteps - 1) done(lane);
+  }
+
+  // K-loop hook, right after the barrier.
+  __device__ __forceinline__ void after_barrier(const KernelArgs& a, int wave, int lane) {
+    (void)a;
+    store_pending(lane);
+    if (!uni(active)) return;
+    if (uni(fetched) > uni(read)) read_back_at(landing(wave, uni(read)), lane);
+    if (uni(fetched) < kSteps) fetch(wave);
+  }
+  // After a K loop: the copy steps the loop did not finish.  The ring and
+  // this wave's staging area are idle until this wave's epilogue (every
+  // wave passed the loop's closing barrier; the staging area is the wave's
+  // own), so all remaining fetches go out at once, into the staging area,
+  // and the drain waits for memory once.  A step fetched by the loop but not
+  // yet read back is still in its landing slot.
   __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
     (void)a;
     asm volatile("" : "+v"(lane));  // (as in begin: lane offsets computed here, not spilled)
-    if (uni(folding)) {  // (a K loop always runs its compute parts; kept for safety)
-      compute<0>(lane);
-      compute<1>(lane);
-      compute<2>(lane);
-    }
     store_pending(lane);
     if (!uni(active)) return;
     const int f0 = uni(fetched);
@@ -520,11 +418,8 @@ struct TileConsumer {
     fetched = kSteps;
     wait_vmcnt<0>();
     while (uni(active)) {
-      const int j = uni(folded);
+      const int j = uni(read);
       read_back_at(j < f0 ? landing(wave, j) : drain_slot(wave, j), lane);
-      compute<0>(lane);
-      compute<1>(lane);
-      compute<2>(lane);
       store_pending(lane);
     }
   }

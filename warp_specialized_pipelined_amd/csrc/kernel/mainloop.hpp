@@ -140,15 +140,11 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 // phases of the K loop stay in the order written.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Work that rides along in the K loop.  Once per iteration, right after the
-// barrier (before the iteration's stage loads), after_barrier() issues what
-// the work needs from memory; its arithmetic comes in pieces,
-// compute<P>() for P = 0 .. 2, placed between the MFMAs that follow, so that
-// it fills issue slots instead of holding the MFMA pipe.
+// Work that rides along in the K loop: once per iteration, right after the
+// barrier (before the iteration's stage loads), after_barrier() issues its
+// memory operations.
 struct NoSideWork {
   __device__ __forceinline__ void after_barrier(const KernelArgs&, int, int) {}
-  template <int P>
-  __device__ __forceinline__ void compute(int) {}
 };
 
 // Stage geometry for element size ES.
@@ -531,9 +527,6 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
         if constexpr (m < 8) la.template load<kMask>(ra, krem_a, cur, wave, m);
         else lb.template load<kMask>(rb, krem_b, cur + kB, wave, m - 8);
       }
-      if constexpr (m == 9) side.template compute<0>(lane);
-      if constexpr (m == 11) side.template compute<1>(lane);
-      if constexpr (m == 13) side.template compute<2>(lane);
     });
   };
   // Iteration d loads stage d+2 (bf16: and B of stage d+1).  While those
