@@ -82,7 +82,8 @@ def test_tile_consumer_workload_8192(mode):
     (300, 300, 264, 0),       # N = 300: a partial 16-byte chunk at the row end
     (1024, 1024, 520, 1),     # one workgroup: 16 tiles through a 2-slot ring
     (1024, 1280, 1000, 3),    # uneven tiles per workgroup
-    (768, 768, 8, 2),         # K shorter than the consumer's 33 steps
+    (768, 768, 8, 2),         # K shorter than the overlapped copy's 33 steps
+    (520, 600, 0, 2),         # K = 0: D = beta * C, still handed off tile by tile
 ])
 @pytest.mark.parametrize("mode", MODES)
 def test_tile_consumer_shapes(M, N, K, mw, mode):
