@@ -92,6 +92,8 @@ def _draw_bf16(gen, shape, dist, K):
 
 def _draw_e4m3(gen, shape):
     x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if x.numel() == 0:   # an empty operand (K = 0): nothing to scale
+        return x.to(torch.float8_e4m3fn), 1.0
     scale = (x.abs().max() / E4M3_MAX).to(torch.float32)
     q = (x / scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
     return q, float(scale)
