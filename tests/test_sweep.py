@@ -14,7 +14,7 @@ from tests.test_batched import Batched, run
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = 160
 
 
 def draw(i):
