@@ -201,9 +201,9 @@ int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* 
 /* gemm_run, and in the same kernel a consumer stage fed through a 2-slot
  * tile hand-off ring: every finished 256 x 256 tile of D is committed by the
  * waves that stored it; the consumer work waits for the commit, reads the
- * tile (as staged in LDS by the epilogue, or -- with
- * MIGEMM_F_CONSUMER_OVERLAP, while the next tile's main loop runs -- back
- * from D), and then releases the slot.  For
+ * tile as the epilogue staged it in LDS (with MIGEMM_F_CONSUMER_OVERLAP the
+ * copy instead reads it back from D while the next tile's main loop runs),
+ * and then releases the slot.  For
  * the tile at tile column t = n / 256 it writes, for each row r of the tile,
  * over the bf16 values x_j = D[r][256t + j], j = 0 .. 255 (columns at or
  * past N read as +0.0 for the sum and are left out of the maximum):
