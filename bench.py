@@ -387,6 +387,27 @@ def main():
         extra["share_8192x1024x8192_stream_k_tflops"] = round(flops_s / (ms_s * 1e-3) / 1e12, 1)
         extra["share_8192x1024x8192_stream_k_tiles"] = int(plan_s.info.stream_k_tiles)
         del ps, Ds, ws
+        # 2048 x 2048 x 8192: 64 tiles, each split over four workgroups by
+        # the stream-K plan (the cost model's choice), whole tiles beside it.
+        log("[bench] drawing inputs for 2048x2048x8192")
+        g = torch.Generator().manual_seed(82)
+        pm = Problem.random(g, 2048, 2048, 8192, "row", "row", dist="normal").to_device()
+        Dm = pm.new_d(0.0)
+        plan_mw = migemm.Plan(pm.desc())
+        plan_ms = migemm.Plan(pm.desc(flags=migemm.MIGEMM_F_STREAM_K))
+        wsm = None
+        if plan_ms.workspace_size:
+            wsm = torch.empty(plan_ms.workspace_size, dtype=torch.uint8, device="cuda")
+            migemm.gemm_workspace_init(plan_ms.handle, wsm)
+        flops_m = 2.0 * pm.M * pm.N * pm.K
+        ms_mw = time_calls(lambda: migemm.gemm_run(plan_mw.handle, pm.dA, pm.dB, None, Dm, 1.0, 0.0,
+                                                   None, stream), n_s, w_s, stream)
+        ms_ms = time_calls(lambda: migemm.gemm_run(plan_ms.handle, pm.dA, pm.dB, None, Dm, 1.0, 0.0,
+                                                   wsm, stream), n_s, w_s, stream)
+        extra["gemm_2048x2048x8192_whole_tiles_tflops"] = round(flops_m / (ms_mw * 1e-3) / 1e12, 1)
+        extra["gemm_2048x2048x8192_stream_k_tflops"] = round(flops_m / (ms_ms * 1e-3) / 1e12, 1)
+        extra["gemm_2048x2048x8192_stream_k_tiles"] = int(plan_ms.info.stream_k_tiles)
+        del pm, Dm, wsm
 
     out = {
         "metric": "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 8192^3, fp8) on 1 GPU",
