@@ -158,9 +158,10 @@ def gemm_entries(M, N, K, A: Operand, B: Operand, C: Operand | None, alpha: floa
 
 
 def tile_rowstats(D_codes: np.ndarray, M: int, N: int, d_rs: int, d_cs: int, tile_n: int = 256):
-    """Row sums and row maxima per tile_n-wide slice of a bf16 D, in the
-    order orc_tile_rowstats states (8-column sequential chunk sums, then a
-    balanced binary tree over the chunks; max ignoring NaN with -0 < +0).
+    """Row sums and row maxima per tile_n-wide slice of a bf16 D, as
+    orc_tile_rowstats defines them: the sequential fp32 sum in ascending
+    column order from +0.0, and the IEEE maximumNumber (NaN ignored, -0 < +0,
+    -inf when the slice holds no number).
     Returns (row_sum, row_max), float32 [M, ceil(N/tile_n)]."""
     lib = _load()
     D_codes = np.ascontiguousarray(D_codes).reshape(-1).view(np.uint16)
@@ -178,7 +179,8 @@ def bf16_codes_to_f64(codes: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 codes (uint16) to float64: the code is the top
     half of a binary32."""
     c = np.asarray(codes).view(np.uint16).astype(np.uint32) << 16
-    return c.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # signalling-NaN codes widen to NaN
+        return c.view(np.float32).astype(np.float64)
 
 
 def check(D_values, ref, absum, in_dtype: int, alpha: float):

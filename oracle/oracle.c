@@ -30,7 +30,8 @@
  *
  * The consumer stage of the tile hand-off (row sum and row max over each
  * 256-wide slice of D, and a bit copy of D) is recomputed from the GPU's own
- * D by orc_tile_rowstats, in the fixed order stated there.
+ * D by orc_tile_rowstats: a sequential fp32 sum in ascending column order and
+ * an IEEE maximumNumber, as defined there.
  */
 #include <math.h>
 #include <stdint.h>
@@ -188,48 +189,40 @@ static float max_signed_zero(float a, float b) {
 }
 
 /* Consumer-stage recompute from a bf16 D (row stride d_rs, column stride
- * d_cs, in elements).  The pages leave the consumer's arithmetic open; this
- * is the order it is defined by here.  For every row r and every slice t of
- * tile_n columns (tile_n a power of two, at least 8), with ld = ceil(N /
- * tile_n) and columns past N-1 read as +0.0:
- *   chunk k of the slice (its columns 8k .. 8k+7, values x0 .. x7):
- *       c_k = (((x0 + x1) + x2) + ... ) + x7                      in fp32
- *   row_sum[r*ld + t] = balanced binary tree over c_0 .. c_{n-1}, n = tile_n/8:
- *       level by level, c_i <- c_{2i} + c_{2i+1}, until one value is left
- *   row_max[r*ld + t] = the largest value of the slice's columns below N that
- *       is not a NaN, with -0 < +0; -inf if there is none.
+ * d_cs, in elements).  The hand-off protocol leaves the consumer's work open
+ * ("do something with the tile"); the work checked here is a per-row fp32 sum
+ * and maximum over each tile_n-wide slice of D, recomputed from the GPU's own
+ * D, so it has exactly one correct value.  Its definition, written out:
+ *
+ *   for every row r and slice t (columns j0 = t*tile_n .. j1-1, with
+ *   j1 = min(N, j0 + tile_n); ld = ceil(N / tile_n)):
+ *     s = +0.0f;  for j = j0, j0+1, ..., j1-1:  s = fl32(s + x_j)
+ *     m = -inf;   for the same j, skipping NaN: m = maximumNumber(m, x_j)
+ *     row_sum[r*ld + t] = s,  row_max[r*ld + t] = m
+ *
+ * where x_j is the bf16 value of D[r][j] widened exactly to fp32.  The sum is
+ * the plain sequential fp32 sum in ascending column order, one rounding per
+ * addition; the maximum is IEEE 754-2019 maximumNumber, which ignores NaN and
+ * orders -0 below +0, so it too has one correct result (-inf when the slice
+ * holds no number).
  * Returns 0, or -1 on a bad argument. */
 int orc_tile_rowstats(int64_t M, int64_t N, const uint16_t* D, int64_t d_rs, int64_t d_cs,
                       int64_t tile_n, float* row_sum, float* row_max) {
-  if (M < 0 || N < 0 || tile_n < 8 || tile_n > 4096 || (tile_n & (tile_n - 1)) != 0) return -1;
+  if (M < 0 || N < 0 || tile_n < 1) return -1;
   int64_t ld = (N + tile_n - 1) / tile_n;
-  int64_t nchunk = tile_n / 8;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < M; ++r) {
-    float c[512];
     for (int64_t t = 0; t < ld; ++t) {
+      int64_t j0 = t * tile_n;
+      int64_t j1 = j0 + tile_n < N ? j0 + tile_n : N;
+      volatile float s = 0.0f; /* volatile: one rounding per addition, in order */
       float m = -INFINITY;
-      for (int64_t k = 0; k < nchunk; ++k) {
-        volatile float s = 0.0f; /* volatile: one rounding per addition, in order */
-        for (int64_t e = 0; e < 8; ++e) {
-          int64_t j = t * tile_n + 8 * k + e;
-          float v = j < N ? (float)orc_bf16_value(D[r * d_rs + j * d_cs]) : 0.0f;
-          if (e == 0) {
-            s = v;
-          } else {
-            s = s + v;
-          }
-          if (j < N && !isnan(v)) m = max_signed_zero(m, v);
-        }
-        c[k] = s;
+      for (int64_t j = j0; j < j1; ++j) {
+        float v = (float)orc_bf16_value(D[r * d_rs + j * d_cs]);
+        s = s + v;
+        if (!isnan(v)) m = max_signed_zero(m, v);
       }
-      for (int64_t n = nchunk; n > 1; n /= 2) {
-        for (int64_t i = 0; i < n / 2; ++i) {
-          volatile float v = c[2 * i] + c[2 * i + 1];
-          c[i] = v;
-        }
-      }
-      row_sum[r * ld + t] = c[0];
+      row_sum[r * ld + t] = s;
       row_max[r * ld + t] = m;
     }
   }

@@ -71,6 +71,25 @@ def test_bf16_decoder_closed_forms():
     assert math.isnan(oracle.bf16_value(0x7FC0))
 
 
+def test_bf16_widening_of_gpu_results_all_codes():
+    """bf16_codes_to_f64 (which widens every GPU D before the acceptance
+    check) against the exact decoder over all 65,536 codes: equal values with
+    equal signs (so -0 stays -0), NaN exactly for the NaN codes."""
+    allc = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_codes_to_f64(allc)
+    want = np.array([oracle.bf16_value(int(c)) for c in allc], dtype=np.float64)
+    nan_codes = ((allc & 0x7F80) == 0x7F80) & ((allc & 0x7F) != 0)
+    assert np.array_equal(np.isnan(got), nan_codes)
+    assert np.array_equal(np.isnan(want), nan_codes)
+    ok = ~nan_codes
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+    # spot values from the format: 0x3F80 = 1, 0xC000 = -2, 0x0001 = 2^-133,
+    # 0x7F7F = (2 - 2^-7) 2^127, 0xFF80 = -inf
+    spot = oracle.bf16_codes_to_f64(np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0xFF80], np.uint16))
+    assert spot.tolist() == [1.0, -2.0, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, -np.inf]
+
+
 def test_e4m3_decoder_all_codes_match_torch():
     allc = np.arange(256, dtype=np.uint8)
     want = torch.from_numpy(allc.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -357,42 +376,88 @@ def bf16_codes(vals):
     return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def chunks_row(chunk_vals, n_chunks=32):
-    """A 256-column row whose chunk k (8 columns) holds eight copies of
-    chunk_vals.get(k, 0)."""
-    row = []
-    for k in range(n_chunks):
-        row += [chunk_vals.get(k, 0.0)] * 8
-    return row
+def rsum(vals, N=None, tile_n=256):
+    """The oracle's row sums of one row of values (bf16-exact), all slices."""
+    N = len(vals) if N is None else N
+    s, _ = oracle.tile_rowstats(bf16_codes([vals]), 1, N, N, 1, tile_n)
+    return s[0]
 
 
-def test_rowstats_sum_order():
+def test_rowstats_sum_is_sequential_in_column_order():
+    """Closed forms of the sequential fp32 sum from +0.0 in ascending column
+    order, on rows where a pairwise or tree order, the reverse order, an fp64
+    accumulator or another start value would each give a different result."""
+    tiny = 2.0 ** -24
     # all ones: 256 in any order
-    s, m = oracle.tile_rowstats(bf16_codes([[1.0] * 256]), 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(256.0) and m[0, 0] == np.float32(1.0)
-    # chunk 0 = [2^24, 1 x 7]: summed in column order inside the chunk, each
-    # +1 rounds back to 2^24 (ties to even); the other 31 chunks are 8 each and
-    # reach the total exactly: 2^24 + 248.  (A plain column-order sum would
-    # give 2^24; a tree inside the chunk would keep 6 of the 7 ones.)
-    row = [2.0 ** 24] + [1.0] * 255
-    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(2.0 ** 24 + 248)
-    # chunk 0 = [1 x 7, 2^24]: 7 + 2^24 rounds to 2^24 + 8, then + 248.
-    row = [1.0] * 7 + [2.0 ** 24] + [1.0] * 248
-    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(2.0 ** 24 + 256)
-    # adjacent chunks pair first: c0 = 2^24 (8 x 2^21), c1 = c17 = 1 (8 x 1/8).
-    # c0 + c1 loses its 1 before c17's 1 arrives, so the total is 2^24; pairing
-    # chunk i with chunk i+16 would add 1 + 1 first and give 2^24 + 2.
-    row = chunks_row({0: 2.0 ** 21, 1: 0.125, 17: 0.125})
-    s, _ = oracle.tile_rowstats(bf16_codes([row]), 1, 256, 256, 1, 256)
-    assert s[0, 0] == np.float32(2.0 ** 24)
-    # signed zeros: a full slice of -0 sums to -0; a slice cut short by N is
-    # padded with +0, and -0 + +0 = +0.
-    s, m = oracle.tile_rowstats(bf16_codes([[-0.0] * 256]), 1, 256, 256, 1, 256)
-    assert s.view(np.uint32)[0, 0] == 0x80000000 and m.view(np.uint32)[0, 0] == 0x80000000
-    s, _ = oracle.tile_rowstats(bf16_codes([[-0.0] * 300]), 1, 300, 300, 1, 256)
-    assert s.view(np.uint32)[0, 1] == 0x00000000
+    assert rsum([1.0] * 256)[0] == np.float32(256.0)
+    # 1 first, then 255 x 2^-24: each addition is half an ulp of 1 and rounds
+    # back to 1 (ties to even), so the sum stays 1.  Pairwise or tree orders
+    # add the small values among themselves first (to 127.5 ulps of 1), and
+    # fp64 keeps them: both give 1 + 2^-16.
+    assert rsum([1.0] + [tiny] * 255)[0] == np.float32(1.0)
+    # the same values with the 1 last: the small ones add exactly to
+    # 255 x 2^-24 first, and 1 + 127.5 ulps rounds to 1 + 128 ulps = 1 + 2^-16.
+    # (A descending order would give 1.)
+    assert rsum([tiny] * 255 + [1.0])[0] == np.float32(1.0 + 2.0 ** -16)
+    # 2^24 first, then 255 ones: every + 1 is half an ulp of 2^24 and rounds
+    # back (ties to even): 2^24.
+    assert rsum([2.0 ** 24] + [1.0] * 255)[0] == np.float32(2.0 ** 24)
+    # 255 ones first (exactly 255), then 2^24: 2^24 + 255 lies halfway between
+    # 2^24 + 254 and 2^24 + 256 and rounds to the even one, 2^24 + 256.
+    assert rsum([1.0] * 255 + [2.0 ** 24])[0] == np.float32(2.0 ** 24 + 256)
+    # the position of the large value decides how many ones survive: with
+    # 2^24 at column 100 the first 100 ones add exactly (100), 2^24 + 100 is
+    # exact (even), and the 155 ones after it each round away.
+    row = [1.0] * 100 + [2.0 ** 24] + [1.0] * 155
+    assert rsum(row)[0] == np.float32(2.0 ** 24 + 100)
+
+
+def test_rowstats_sum_starts_at_plus_zero_and_covers_valid_columns_only():
+    # from +0.0: +0 + (-0) = +0, so a slice of negative zeros sums to +0
+    # (starting from the first value would keep -0)
+    s = rsum([-0.0] * 256)
+    assert s.view(np.uint32)[0] == 0x00000000
+    # a slice cut short by N covers only its columns: 300 columns give a
+    # second slice of 44 values
+    row = [0.5] * 256 + [0.25] * 44
+    s = rsum(row)
+    assert s[0] == np.float32(128.0) and s[1] == np.float32(11.0)
+    # slices never mix: a huge value in slice 0 does not absorb slice 1
+    row = [2.0 ** 24] + [0.0] * 255 + [1.0] * 3
+    s = rsum(row)
+    assert s[0] == np.float32(2.0 ** 24) and s[1] == np.float32(3.0)
+    # NaN and infinities propagate through the sum as IEEE addition says
+    assert np.isnan(rsum([1.0, float("nan")] + [0.0] * 254)[0])
+    assert rsum([float("inf")] + [1.0] * 255)[0] == np.float32(np.inf)
+    assert np.isnan(rsum([float("inf"), float("-inf")] + [0.0] * 254)[0])
+    # other slice widths follow the same definition
+    s, _ = oracle.tile_rowstats(bf16_codes([[1.0] + [2.0 ** -24] * 7]), 1, 8, 8, 1, 8)
+    assert s[0, 0] == np.float32(1.0)
+
+
+def test_rowstats_sum_brute_force_on_random_rows():
+    """Against a step-by-step numpy fp32 recurrence (one float32 addition per
+    column, in column order), on rows whose magnitudes span many binades so
+    that any other order or precision rounds differently somewhere."""
+    rng = np.random.default_rng(7)
+    M, N = 40, 700
+    vals = rng.standard_normal((M, N)) * np.exp2(rng.integers(-20, 20, (M, N)))
+    D = bf16_codes(vals.tolist())
+    s, _ = oracle.tile_rowstats(D, M, N, N, 1, 256)
+    x = torch.from_numpy(D.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    x = x.reshape(M, N)
+    differs_from_pairwise = 0
+    for r in range(M):
+        for t in range(3):
+            seg = x[r, 256 * t: min(N, 256 * t + 256)]
+            acc = np.float32(0.0)
+            for v in seg:
+                acc = np.float32(acc + v)
+            assert s[r, t].view(np.uint32) == acc.view(np.uint32), (r, t)
+            differs_from_pairwise += int(np.float32(np.sum(seg)) != acc)
+    # the rows are chosen so that numpy's pairwise sum differs often: the pin
+    # would catch a pairwise oracle
+    assert differs_from_pairwise > 20
 
 
 def test_rowstats_max_rules():

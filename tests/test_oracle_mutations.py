@@ -13,7 +13,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
-# (name, text in oracle.c, replacement): one plausible mistake each.
+# (name, text in oracle.c, replacement[, text, replacement ...]): one plausible
+# mistake each.
 MUTATIONS = [
     ("bf16_bias", "ldexp((double)(128 + f), e - 127 - 7)", "ldexp((double)(128 + f), e - 126 - 7)"),
     ("bf16_subnormal", "ldexp((double)f, 1 - 127 - 7)", "ldexp((double)f, 0 - 127 - 7)"),
@@ -35,24 +36,34 @@ MUTATIONS = [
     ("entries_c_transposed", "    if (beta != 0.0) r += beta * elem(c_type, C, c_rs, c_cs, i, j);\n    ref[e] = r;",
      "    if (beta != 0.0) r += beta * elem(c_type, C, c_cs, c_rs, i, j);\n    ref[e] = r;"),
     ("rowsum_in_double", "volatile float s = 0.0f;", "volatile double s = 0.0;"),
+    ("rowsum_from_minus_zero", "volatile float s = 0.0f;", "volatile float s = -0.0f;"),
+    ("rowsum_descending", "      for (int64_t j = j0; j < j1; ++j) {\n        float v",
+     "      for (int64_t j = j1 - 1; j >= j0; --j) {\n        float v"),
+    ("rowsum_two_partials",
+     "        s = s + v;\n        if (!isnan(v)) m = max_signed_zero(m, v);\n      }\n      row_sum[r * ld + t] = s;",
+     "        if (((j - j0) & 1) == 0) s = s + v; else s2 = s2 + v;\n"
+     "        if (!isnan(v)) m = max_signed_zero(m, v);\n      }\n      row_sum[r * ld + t] = s + s2;",
+     "      float m = -INFINITY;\n", "      float m = -INFINITY;\n      volatile float s2 = 0.0f;\n"),
+    ("rowsum_skips_last_column", "      for (int64_t j = j0; j < j1; ++j) {\n        float v",
+     "      for (int64_t j = j0; j + 1 < j1; ++j) {\n        float v"),
     ("rowmax_from_zero", "float m = -INFINITY;", "float m = 0.0f;"),
-    ("rowstats_short_chunk", "for (int64_t e = 0; e < 8; ++e) {", "for (int64_t e = 0; e < 7; ++e) {"),
-    ("tree_strided_pairs", "volatile float v = c[2 * i] + c[2 * i + 1];", "volatile float v = c[i] + c[i + n / 2];"),
     ("max_signed_zero_ignored", "return signbit(a) ? b : a;", "return a;"),
-    ("max_keeps_nan", "if (j < N && !isnan(v)) m = max_signed_zero(m, v);", "if (j < N) m = max_signed_zero(m, v);"),
-    ("pad_with_minus_zero", "(float)orc_bf16_value(D[r * d_rs + j * d_cs]) : 0.0f;",
-     "(float)orc_bf16_value(D[r * d_rs + j * d_cs]) : -0.0f;"),
+    ("max_keeps_nan", "if (!isnan(v)) m = max_signed_zero(m, v);", "m = max_signed_zero(m, v);"),
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(name, old, new):
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(mutation):
+    # (name, old, new[, old2, new2 ...]): every `old` must occur once
+    name, pairs = mutation[0], list(zip(mutation[1::2], mutation[2::2]))
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+    for old, new in pairs:
+        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+        src = src.replace(old, new)
     with tempfile.TemporaryDirectory() as d:
         msrc = os.path.join(d, "oracle_mut.c")
         lib = os.path.join(d, "liboracle_mut.so")
-        open(msrc, "w").write(src.replace(old, new))
+        open(msrc, "w").write(src)
         subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11",
                         "-o", lib, msrc, "-lm"], check=True)
         env = dict(os.environ, MIGEMM_ORACLE_LIB=lib)
