@@ -205,17 +205,17 @@ int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* 
  * copy instead reads it back from D while the next tile's main loop runs),
  * and then releases the slot.  For
  * the tile at tile column t = n / 256 it writes, for each row r of the tile,
- * over the bf16 values x_j = D[r][256t + j], j = 0 .. 255 (columns at or
- * past N read as +0.0 for the sum and are left out of the maximum):
- *   row_sum[r * ceil(N/256) + t] = fp32 sum in a fixed order: chunk sums
- *       c_k = (((x_8k + x_8k+1) + x_8k+2) + ...) + x_8k+7, k = 0 .. 31, then
- *       a balanced binary tree over c_0 .. c_31, adjacent pairs first
- *       (c_0 + c_1, c_2 + c_3, ...; then pairs of those; ...),
+ * over the bf16 values x_j = D[r][256t + j] of the columns below N, widened
+ * exactly to fp32:
+ *   row_sum[r * ceil(N/256) + t] = s, the plain sequential fp32 sum in
+ *       ascending column order: s = +0.0f, then s = s + x_j for j = 0, 1, ...
+ *       (one rounding per addition),
  *   row_max[r * ceil(N/256) + t] = the largest x_j that is not a NaN, with
- *       -0 < +0; -inf if there is none,
- * and copies the tile bit for bit into D_copy (same strides as D).  (The
- * pages leave the consumer's arithmetic open; this order lets 32 lanes
- * share a row.)
+ *       -0 < +0 (IEEE 754-2019 maximumNumber); -inf if there is none,
+ * and copies the tile bit for bit into D_copy (same strides as D).  Both
+ * statistics therefore have exactly one correct value given D.  (The hand-off
+ * issue leaves the consumer's work open -- "do something with the tile";
+ * these are the statistics this library's consumer stage computes.)
  * row_sum and row_max are M x ceil(N/256) fp32, row-major, 4-byte aligned;
  * D_copy is 16-byte aligned and must not overlap D.  Requires a plan created
  * with MIGEMM_F_TILE_CONSUMER and a row-major D. */

@@ -34,16 +34,15 @@
 // its own.
 //
 // Consumer work for a 256 x 256 tile at tile column t: for each of its rows r,
-// over the tile's columns (those past N read as +0.0 for the sum and are left
-// out of the max), in an order fixed so that it can be checked bit for bit:
-//   chunk k = columns 8k .. 8k+7:  c_k = (((x0 + x1) + x2) + ...) + x7   (fp32)
-//   row_sum[r][t] = balanced binary tree over c_0 .. c_31, adjacent pairs
-//                   first (c_0 + c_1, c_2 + c_3, ...; then pairs of those, ...)
-//   row_max[r][t] = the largest non-NaN value, with -0 < +0; -inf if none,
-// and the row is copied bit for bit to D_copy.  (The pages leave the
-// consumer's arithmetic open; this order lets 32 lanes share a row, as the
-// overlapped schedule does, and gives the same bits when one lane folds the
-// whole row, as the staged schedule does.)
+// over the tile's columns below N, with x_j the bf16 value of D[r][256t + j]
+// widened to fp32:
+//   row_sum[r][t] = s, where s = +0.0f and then s = s + x_j for j = 0, 1, ...
+//                   in column order (one fp32 rounding per addition),
+//   row_max[r][t] = the largest x_j that is not a NaN, with -0 < +0; -inf if
+//                   there is none (IEEE 754-2019 maximumNumber),
+// and the row is copied bit for bit to D_copy.  Both statistics have exactly
+// one correct value given D.  One lane folds one whole row, so the sequential
+// order costs no more additions than any other.
 #pragma once
 
 #include "gfx950.hpp"
@@ -139,8 +138,7 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 //
 // The row statistics are folded right after the tile's commit, from the
 // tile as the epilogue left it staged in LDS, one row per lane: lane L folds
-// row 64 w + L alone -- its 32 chunk sums, then the balanced tree over them
-// in registers.  The 16 rows that one read touches at the staging area's
+// row 64 w + L alone, column after column.  The 16 rows that one read touches at the staging area's
 // 272-byte pitch hit every bank once.  The statistics leave with one store
 // per array (64 lanes, one entry each).
 //
@@ -265,66 +263,54 @@ struct TileConsumer {
     return q * kStagingWaveBytes + (row & 127) * kStagingRowBytes + (col & 127) * 2;
   }
 
-  // The sum (in column order) and maximum key of a chunk of 8 columns with
-  // n valid columns from its first (n >= 8 whenever the tile is whole).
-  __device__ __forceinline__ void chunk_fold(const u32x4& x, int n, float& s_out,
-                                             int32_t& mk_out) const {
-    float s;
-    int32_t mk;
+  // Adds a chunk of 8 columns to a row's running sum, one column at a time in
+  // column order, and to its running maximum key.  n = the chunk's valid
+  // columns from its first (n >= 8 whenever the tile is whole); columns past
+  // N are left out of both.
+  __device__ __forceinline__ void fold_chunk(const u32x4& x, int n, float& s, int32_t& mk) const {
     if (__builtin_expect(ncols == kTileN, 1)) {
       // A whole row slice: no column checks; the maximum on both halves
       // of each word at once.
-      s = bf16_lo(x[0]);
-      s = s + bf16_hi(x[0]);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
+      for (int w = 0; w < 4; ++w) {
         s = s + bf16_lo(x[w]);
         s = s + bf16_hi(x[w]);
       }
       s16x2 m2 = max_keys2(x[0]);
 #pragma unroll
       for (int w = 1; w < 4; ++w) m2 = __builtin_elementwise_max(m2, max_keys2(x[w]));
-      mk = max((int32_t)m2.x, (int32_t)m2.y);
+      mk = max(mk, max((int32_t)m2.x, (int32_t)m2.y));
     } else {
-      s = 0.0f;
-      mk = kNoKey;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t h = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFF;
-        const float y = e < n ? __uint_as_float(h << 16) : 0.0f;
-        s = e == 0 ? y : s + y;
-        mk = max(mk, e < n ? max_key(h) : kNoKey);
+        if (e < n) {
+          s = s + __uint_as_float(h << 16);
+          mk = max(mk, max_key(h));
+        }
       }
     }
-    s_out = s;
-    mk_out = mk;
   }
 
   // The row statistics of the tile the epilogue has just staged (every wave
   // staged its quarter, and the ring is refilled only after the caller's
   // next barrier; the wait in begin() saw all four waves commit, which
-  // orders their staging writes before these reads).
+  // orders their staging writes before these reads).  Lane L folds row
+  // 64 w + L: s = +0.0f, then s = s + x_j for j = 0, 1, ..., in column order.
   __device__ __forceinline__ void fold_staged(int wave, int lane) {
     asm volatile("" : "+v"(lane));  // (as in begin)
     const int row = wave * 64 + lane;
     const uint32_t base = 2 * (row >> 7) * kStagingWaveBytes + (row & 127) * kStagingRowBytes;
     constexpr int kChunks = kTileN / 8;
-    float c[kChunks];
+    float s = 0.0f;
     int32_t mk = kNoKey;
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
       const u32x4 x = *(const MIGEMM_LDS u32x4*)lds_at(
           base + (k / (kChunks / 2)) * kStagingWaveBytes + (k % (kChunks / 2)) * 16);
-      int32_t m;
-      chunk_fold(x, ncols - 8 * k, c[k], m);
-      mk = max(mk, m);
+      fold_chunk(x, ncols - 8 * k, s, mk);
     }
-    // The balanced tree, adjacent chunks first.
-#pragma unroll
-    for (int w = 1; w < kChunks; w *= 2)
-#pragma unroll
-      for (int k = 0; k < kChunks; k += 2 * w) c[k] = c[k] + c[k + w];
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[0]), rsum, stat_lane_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), rsum, stat_lane_off, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(max_key_value(mk)), rmax,
                                           stat_lane_off, 0, 0);
   }
