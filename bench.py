@@ -80,14 +80,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the plain/fp8 side measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-baseline duration")
-    ap.add_argument("--variant", choices=["full", "consumer", "plain", "fp8", "copy"], default="full",
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="untimed back-to-back steps before the warm-up, for steady clocks")
+    ap.add_argument("--variant", choices=["full", "consumer", "overlap", "plain", "fp8", "cfg1", "cfg2",
+                                          "cfg3", "copy"], default="full",
                     help="profiling runs: time one kernel only and print a short line "
                          "(copy = a plain 128 MiB device copy, the byte-counter calibration)")
     return ap.parse_args()
 
 
+VARIANTS = {"consumer": 3, "overlap": 3, "plain": 3, "fp8": 4, "cfg1": 0, "cfg2": 1, "cfg3": 2}
+
+
 def run_variant(args):
-    """One kernel, timed alone (for rocprofv3 counter passes)."""
+    """One kernel, timed alone (for rocprofv3 counter passes): the 8192^3
+    bf16 workload with the tile consumer (staged or overlapped schedule) or
+    plain, the e4m3 workload, one of the three smaller workloads, or a
+    128 MiB device copy (the byte-counter calibration)."""
     import torch
     from warp_specialized_pipelined_amd import migemm, synth
     from tests.helpers import Problem
@@ -100,11 +109,14 @@ def run_variant(args):
         print(json.dumps({"variant": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "ms": round(ms, 4), "GB/s": round(4 * n / (ms * 1e-3) / 1e9, 1)}))
         return
-    w = synth.WORKLOADS[4] if args.variant == "fp8" else synth.WORKLOADS[3]
+    w = synth.WORKLOADS[VARIANTS[args.variant]]
     p = Problem.from_workload(w).to_device()
     D = p.new_d(0.0)
-    if args.variant == "consumer":
-        plan = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER))
+    if args.variant in ("consumer", "overlap"):
+        flags = migemm.MIGEMM_F_TILE_CONSUMER
+        if args.variant == "overlap":
+            flags |= migemm.MIGEMM_F_CONSUMER_OVERLAP
+        plan = migemm.Plan(p.desc(flags=flags))
         ld = (w.N + 255) // 256
         rs = torch.empty((w.M, ld), dtype=torch.float32, device="cuda")
         rm = torch.empty_like(rs)
@@ -113,7 +125,8 @@ def run_variant(args):
                                                         0.0, rs, rm, Dc, None, stream)
     else:
         plan = migemm.Plan(p.desc())
-        fn = lambda: migemm.gemm_run(plan.handle, p.dA, p.dB, None, D, p.alpha, 0.0, None, stream)
+        fn = lambda: migemm.gemm_run(plan.handle, p.dA, p.dB, p.dC, D, p.alpha, p.beta, None,
+                                     stream)
     ms = time_calls(fn, args.steps, args.warmup, stream)
     print(json.dumps({"variant": args.variant, "workload": w.name, "ms": round(ms, 4),
                       "TFLOP/s": round(w.flops / (ms * 1e-3) / 1e12, 1)}))
@@ -132,6 +145,56 @@ def time_calls(fn, steps, warmup, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps   # ms per call
+
+
+def settle(fn, stream, seconds):
+    """Run `fn` back to back for about `seconds` (untimed): the board's clock
+    and power take ~30 launches of a large GEMM to reach their steady state,
+    which a fresh process has not yet reached after a few warm-up steps."""
+    import torch
+    if seconds <= 0:
+        return
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def per_launch_ms(fn, n, stream):
+    """n back-to-back launches with a HIP event recorded on the launch stream
+    between consecutive ones; returns the n per-launch times in ms."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def summary_us(ms_list):
+    import statistics
+    return {"median_us": round(1e3 * statistics.median(ms_list), 2),
+            "min_us": round(1e3 * min(ms_list), 2),
+            "mean_us": round(1e3 * sum(ms_list) / len(ms_list), 2),
+            "launches": len(ms_list)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def sysfs_gpu_dir():
@@ -234,10 +297,51 @@ def cpu_baseline(p, target_s):
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"first {rows} rows of the {p.M}x{p.N}x{p.K} product (all columns, full K), "
                   f"fp64 accumulation, {t:.1f} s",
     }
+
+
+def algorithmic_bytes(w, consumer=False):
+    """Bytes the method must move per launch: A and B read once, D written
+    once, C read once when beta != 0; the tile consumer adds the copy
+    (MN x 2) and the two statistics arrays (2 M ceil(N/256) x 4)."""
+    es = 2 if w.dtype == 1 else 1
+    b = (w.M * w.K + w.K * w.N) * es + w.M * w.N * 2
+    if w.beta != 0.0:
+        b += w.M * w.N * 2
+    if consumer:
+        b += w.M * w.N * 2 + 2 * w.M * ((w.N + 255) // 256) * 4
+    return b
+
+
+def config_figures(w, ms_list, consumer=False):
+    """Median/min time of one workload with its roofline: MFMA-bound when its
+    arithmetic intensity is above the ridge point (peak flop/s / 8 TB/s),
+    HBM-bound below it."""
+    import statistics
+    peak = PEAK_BF16_TFLOPS if w.dtype == 1 else PEAK_FP8_TFLOPS
+    med = statistics.median(ms_list)
+    tflops = w.flops / (med * 1e-3) / 1e12
+    nbytes = algorithmic_bytes(w, consumer)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    ai = w.flops / nbytes
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if ai >= ridge else "hbm"
+    out = summary_us(ms_list)
+    out.update({
+        "shape": f"{w.M}x{w.N}x{w.K}", "dtype": "bf16" if w.dtype == 1 else "e4m3",
+        "layouts": f"A {w.a_layout}, B {w.b_layout}", "alpha": w.alpha, "beta": w.beta,
+        "tflops_at_median": round(tflops, 1), "mfma_peak_tflops": round(peak, 1),
+        "frac_of_mfma_peak": round(tflops / peak, 4),
+        "algorithmic_bytes": nbytes, "hbm_gbs_at_median": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "arithmetic_intensity": round(ai, 1), "bound": bound,
+        "frac_of_roofline": round(tflops / peak if bound == "mfma" else gbs / HBM_PEAK_GBS, 4),
+    })
+    return out
 
 
 def main():
@@ -246,6 +350,7 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    import statistics
     import torch
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from warp_specialized_pipelined_amd import migemm, synth
@@ -267,21 +372,13 @@ def main():
     p = Problem.from_workload(w).to_device()
     D = p.new_d(0.0)
     plan_plain = migemm.Plan(p.desc())
-    consumer = False
-    try:
-        plan_cons = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER))
-        stat_ld = (w.N + 255) // 256
-        row_sum = torch.empty((w.M, stat_ld), dtype=torch.float32, device="cuda")
-        row_max = torch.empty((w.M, stat_ld), dtype=torch.float32, device="cuda")
-        D_copy = torch.empty_like(D)
-        st = migemm.gemm_run_with_tile_consumer(plan_cons.handle, p.dA, p.dB, None, D, p.alpha, 0.0,
-                                                row_sum, row_max, D_copy, check=False)
-        torch.cuda.synchronize()
-        consumer = st == migemm.MIGEMM_OK
-        if not consumer:
-            log(f"[bench] tile consumer unavailable: {migemm.gemm_status_string(st)}")
-    except migemm.MigemmError as e:
-        log(f"[bench] tile consumer plan failed: {e}")
+    plan_cons = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER))
+    plan_ov = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER |
+                                 migemm.MIGEMM_F_CONSUMER_OVERLAP))
+    stat_ld = (w.N + 255) // 256
+    row_sum = torch.empty((w.M, stat_ld), dtype=torch.float32, device="cuda")
+    row_max = torch.empty((w.M, stat_ld), dtype=torch.float32, device="cuda")
+    D_copy = torch.empty_like(D)
 
     def step_plain():
         migemm.gemm_run(plan_plain.handle, p.dA, p.dB, None, D, p.alpha, 0.0, None, stream)
@@ -290,8 +387,17 @@ def main():
         migemm.gemm_run_with_tile_consumer(plan_cons.handle, p.dA, p.dB, None, D, p.alpha, 0.0,
                                            row_sum, row_max, D_copy, None, stream)
 
-    step = step_cons if consumer else step_plain
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up (consumer={consumer})")
+    def step_ov():
+        migemm.gemm_run_with_tile_consumer(plan_ov.handle, p.dA, p.dB, None, D, p.alpha, 0.0,
+                                           row_sum, row_max, D_copy, None, stream)
+
+    step = step_cons
+    # The board needs ~30 launches of this GEMM to reach the clock and power
+    # it then holds; a settle run first, so the timed steps measure that
+    # steady state rather than the ramp.
+    n_settle = settle(step, stream, args.settle_seconds)
+    log(f"[bench] settled with {n_settle} untimed steps; timing {args.steps} steps after "
+        f"{args.warmup} warm-up")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ms = time_calls(step, args.steps, args.warmup, stream)
@@ -299,7 +405,10 @@ def main():
     tflops = w.flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step  {tflops:.1f} TFLOP/s  ({wall:.1f} s wall)")
 
-    extra = {"consumer_variant": consumer}
+    extra = {"consumer_schedule": "staged (the default of gemm_run_with_tile_consumer)",
+             "settle_steps": n_settle,
+             "pages_throughput_figures": "none: the pages publish no throughput figures, so there "
+                                         "is no external number to compare with"}
 
     def clock_extras(prefix, fn, ms_step, flops, flop_per_clk_cu):
         """The shader clock under this load (amdgpu's DPM readout), the board
@@ -318,96 +427,105 @@ def main():
         if clk["watts"] is not None:
             extra[prefix + "board_power_w_median"] = round(clk["watts"], 1)
 
-    clock_extras("", step, ms, w.flops, 4096)
     if not args.no_extra:
-        ms_plain = time_calls(step_plain, args.steps, max(2, args.warmup // 2), stream)
-        extra["plain_gemm_ms"] = round(ms_plain, 4)
-        extra["plain_gemm_tflops"] = round(w.flops / (ms_plain * 1e-3) / 1e12, 1)
-        extra["plain_gemm_frac_of_peak"] = round(extra["plain_gemm_tflops"] / PEAK_BF16_TFLOPS, 4)
-        if consumer:
-            extra["consumer_over_plain_time"] = round(ms / ms_plain, 4)
-            clock_extras("plain_gemm_", step_plain, ms_plain, w.flops, 4096)
-            # The other schedule of the consumer stage: inside the next
-            # tile's K loop, on the tile fetched back from D.
-            plan_ov = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER |
-                                         migemm.MIGEMM_F_CONSUMER_OVERLAP))
-            ms_ov = time_calls(lambda: migemm.gemm_run_with_tile_consumer(
-                plan_ov.handle, p.dA, p.dB, None, D, p.alpha, 0.0, row_sum, row_max, D_copy, None,
-                stream), args.steps, max(2, args.warmup // 2), stream)
-            extra["consumer_overlapped_tflops"] = round(w.flops / (ms_ov * 1e-3) / 1e12, 1)
-            extra["consumer_overlapped_over_plain_time"] = round(ms_ov / ms_plain, 4)
+        # Plain GEMM against both schedules of the tile consumer, interleaved
+        # (plain, staged, overlapped) x 5 rounds on the same inputs, so that
+        # clock drift falls on all three alike.
+        n_i = max(10, args.steps // 2)
+        times = {"plain": [], "staged": [], "overlapped": []}
+        fns = {"plain": step_plain, "staged": step_cons, "overlapped": step_ov}
+        for _ in range(5):
+            for name, fn in fns.items():
+                fn()                              # one untimed launch at each switch
+                times[name] += per_launch_ms(fn, n_i, stream)
+        med = {k: statistics.median(v) for k, v in times.items()}
+        extra["interleaved_8192"] = {
+            "order": "(plain, staged consumer, overlapped consumer) x 5 rounds of "
+                     f"{n_i} launches each, per-launch HIP events",
+            "plain": config_figures(w, times["plain"]),
+            "staged": config_figures(w, times["staged"], consumer=True),
+            "overlapped": config_figures(w, times["overlapped"], consumer=True),
+            "staged_over_plain_time": round(med["staged"] / med["plain"], 4),
+            "overlapped_over_plain_time": round(med["overlapped"] / med["plain"], 4),
+        }
+        log(f"[bench] interleaved medians (ms): {med}")
+        extra["plain_gemm_tflops"] = extra["interleaved_8192"]["plain"]["tflops_at_median"]
+        extra["plain_gemm_frac_of_peak"] = extra["interleaved_8192"]["plain"]["frac_of_mfma_peak"]
+        extra["consumer_over_plain_time"] = extra["interleaved_8192"]["staged_over_plain_time"]
+        extra["consumer_overlapped_over_plain_time"] = \
+            extra["interleaved_8192"]["overlapped_over_plain_time"]
+        clock_extras("", step, ms, w.flops, 4096)
+        clock_extras("plain_gemm_", step_plain, med["plain"], w.flops, 4096)
         # The vendor library on the same inputs, for reference only: torch's
         # bf16 matmul (hipBLASLt) of the same row-major A and B, contiguous.
         if p.a_rs == w.K and p.b_rs == w.N and p.a_cs == 1 and p.b_cs == 1:
             A2 = p.dA.view(w.M, w.K)
             B2 = p.dB.view(w.K, w.N)
             out2 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
-            ms_lib = time_calls(lambda: torch.matmul(A2, B2, out=out2), max(10, args.steps // 2),
-                                max(5, args.warmup // 2), stream)
+            lib = lambda: torch.matmul(A2, B2, out=out2)
+            settle(lib, stream, 0.5)
+            ms_lib = statistics.median(per_launch_ms(lib, max(10, args.steps // 2), stream))
             extra["library_gemm_tflops"] = round(w.flops / (ms_lib * 1e-3) / 1e12, 1)
             extra["library_gemm"] = "torch.matmul bf16 (hipBLASLt), same A and B, no consumer"
-            clock_extras("library_gemm_", lambda: torch.matmul(A2, B2, out=out2), ms_lib, w.flops,
-                         4096)
+            clock_extras("library_gemm_", lib, ms_lib, w.flops, 4096)
             del out2
-        # fp8 e4m3 8192 x 8192 x 16384
+        del D_copy, row_sum, row_max
+
+        # Every workload of the set, one after another: gemm_run on its own
+        # plan (the 8192^3 one is the interleaved block above).
+        configs = {}
+        for wc in synth.WORKLOADS:
+            if wc is w:
+                continue
+            log(f"[bench] workload {wc.name}")
+            pc = Problem.from_workload(wc).to_device()
+            Dc = pc.new_d(0.0)
+            plan_c = migemm.Plan(pc.desc())
+            fn = lambda: migemm.gemm_run(plan_c.handle, pc.dA, pc.dB, pc.dC, Dc, pc.alpha,
+                                         pc.beta, None, stream)
+            settle(fn, stream, 0.4)
+            n_c = max(20, args.steps)
+            if wc.M * wc.N * wc.K <= 256 ** 3:
+                n_c = 200                         # a few microseconds each
+            configs[wc.name] = config_figures(wc, per_launch_ms(fn, n_c, stream))
+            if wc.dtype == synth.E4M3:
+                clock_extras("fp8_gemm_", fn, statistics.median(per_launch_ms(fn, 5, stream)),
+                             wc.flops, 8192)
+            del pc, Dc
+        configs[w.name] = extra["interleaved_8192"]["staged"]
+        extra["workloads"] = configs
         w8 = synth.WORKLOADS[4]
-        log(f"[bench] drawing inputs for {w8.name}")
-        p8 = Problem.from_workload(w8).to_device()
-        D8 = p8.new_d(0.0)
-        plan8 = migemm.Plan(p8.desc())
+        extra["fp8_gemm_tflops"] = configs[w8.name]["tflops_at_median"]
+        extra["fp8_gemm_frac_of_peak"] = configs[w8.name]["frac_of_mfma_peak"]
 
-        def step8():
-            migemm.gemm_run(plan8.handle, p8.dA, p8.dB, None, D8, p8.alpha, 0.0, None, stream)
-
-        ms8 = time_calls(step8, max(5, args.steps // 2), max(2, args.warmup // 2), stream)
-        extra["fp8_gemm_ms"] = round(ms8, 4)
-        extra["fp8_gemm_tflops"] = round(w8.flops / (ms8 * 1e-3) / 1e12, 1)
-        extra["fp8_gemm_frac_of_peak"] = round(extra["fp8_gemm_tflops"] / PEAK_FP8_TFLOPS, 4)
-        clock_extras("fp8_gemm_", step8, ms8, w8.flops, 8192)
-        del p8, D8
         # One GPU's share of an 8-way split of N, 8192 x 1024 x 8192 bf16: 128
-        # tiles on 256 compute units, whole tiles against the stream-K plan.
-        log("[bench] drawing inputs for 8192x1024x8192")
-        g = torch.Generator().manual_seed(81)
-        ps = Problem.random(g, 8192, 1024, 8192, "row", "row", dist="normal").to_device()
-        Ds = ps.new_d(0.0)
-        plan_w = migemm.Plan(ps.desc())
-        plan_s = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_STREAM_K))
-        ws = None
-        if plan_s.workspace_size:
-            ws = torch.empty(plan_s.workspace_size, dtype=torch.uint8, device="cuda")
-            migemm.gemm_workspace_init(plan_s.handle, ws)
-        flops_s = 2.0 * ps.M * ps.N * ps.K
-        n_s, w_s = max(10, args.steps // 2), max(5, args.warmup // 2)
-        ms_w = time_calls(lambda: migemm.gemm_run(plan_w.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0,
-                                                  None, stream), n_s, w_s, stream)
-        ms_s = time_calls(lambda: migemm.gemm_run(plan_s.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0,
-                                                  ws, stream), n_s, w_s, stream)
-        extra["share_8192x1024x8192_whole_tiles_tflops"] = round(flops_s / (ms_w * 1e-3) / 1e12, 1)
-        extra["share_8192x1024x8192_stream_k_tflops"] = round(flops_s / (ms_s * 1e-3) / 1e12, 1)
-        extra["share_8192x1024x8192_stream_k_tiles"] = int(plan_s.info.stream_k_tiles)
-        del ps, Ds, ws
-        # 2048 x 2048 x 8192: 64 tiles, each split over four workgroups by
-        # the stream-K plan (the cost model's choice), whole tiles beside it.
-        log("[bench] drawing inputs for 2048x2048x8192")
-        g = torch.Generator().manual_seed(82)
-        pm = Problem.random(g, 2048, 2048, 8192, "row", "row", dist="normal").to_device()
-        Dm = pm.new_d(0.0)
-        plan_mw = migemm.Plan(pm.desc())
-        plan_ms = migemm.Plan(pm.desc(flags=migemm.MIGEMM_F_STREAM_K))
-        wsm = None
-        if plan_ms.workspace_size:
-            wsm = torch.empty(plan_ms.workspace_size, dtype=torch.uint8, device="cuda")
-            migemm.gemm_workspace_init(plan_ms.handle, wsm)
-        flops_m = 2.0 * pm.M * pm.N * pm.K
-        ms_mw = time_calls(lambda: migemm.gemm_run(plan_mw.handle, pm.dA, pm.dB, None, Dm, 1.0, 0.0,
-                                                   None, stream), n_s, w_s, stream)
-        ms_ms = time_calls(lambda: migemm.gemm_run(plan_ms.handle, pm.dA, pm.dB, None, Dm, 1.0, 0.0,
-                                                   wsm, stream), n_s, w_s, stream)
-        extra["gemm_2048x2048x8192_whole_tiles_tflops"] = round(flops_m / (ms_mw * 1e-3) / 1e12, 1)
-        extra["gemm_2048x2048x8192_stream_k_tflops"] = round(flops_m / (ms_ms * 1e-3) / 1e12, 1)
-        extra["gemm_2048x2048x8192_stream_k_tiles"] = int(plan_ms.info.stream_k_tiles)
-        del pm, Dm, wsm
+        # tiles on 256 compute units, whole tiles against the stream-K plan;
+        # and 2048 x 2048 x 8192 (64 tiles, each split four ways).
+        for (M_, N_, K_, seed, key) in ((8192, 1024, 8192, 81, "share_8192x1024x8192"),
+                                        (2048, 2048, 8192, 82, "gemm_2048x2048x8192")):
+            log(f"[bench] drawing inputs for {M_}x{N_}x{K_}")
+            g = torch.Generator().manual_seed(seed)
+            ps = Problem.random(g, M_, N_, K_, "row", "row", dist="normal").to_device()
+            Ds = ps.new_d(0.0)
+            plan_w = migemm.Plan(ps.desc())
+            plan_s = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_STREAM_K))
+            ws = None
+            if plan_s.workspace_size:
+                ws = torch.empty(plan_s.workspace_size, dtype=torch.uint8, device="cuda")
+                migemm.gemm_workspace_init(plan_s.handle, ws)
+            flops_s = 2.0 * M_ * N_ * K_
+            fw = lambda: migemm.gemm_run(plan_w.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0, None,
+                                         stream)
+            fs = lambda: migemm.gemm_run(plan_s.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0, ws,
+                                         stream)
+            settle(fw, stream, 0.2)
+            ms_w = statistics.median(per_launch_ms(fw, max(20, args.steps), stream))
+            settle(fs, stream, 0.2)
+            ms_s = statistics.median(per_launch_ms(fs, max(20, args.steps), stream))
+            extra[key + "_whole_tiles_tflops"] = round(flops_s / (ms_w * 1e-3) / 1e12, 1)
+            extra[key + "_stream_k_tflops"] = round(flops_s / (ms_s * 1e-3) / 1e12, 1)
+            extra[key + "_stream_k_tiles"] = int(plan_s.info.stream_k_tiles)
+            del ps, Ds, ws
 
     out = {
         "metric": "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 8192^3, fp8) on 1 GPU",
@@ -427,7 +545,7 @@ def main():
             "M": w.M, "N": w.N, "K": w.K,
             "a_layout": w.a_layout, "b_layout": w.b_layout,
             "entries": "N(0,1)/sqrt(K) rounded to bf16",
-            "tile_consumer": consumer,
+            "tile_consumer": True,
             "parallelism": "single GPU, persistent grid",
         },
         "roofline": {

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from warp_specialized_pipelined_amd import migemm, synth
-from tests.helpers import Problem, check_full, check_sampled, codes
+from tests.helpers import Problem, check_full, codes, workload_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,10 @@ def test_tile_consumer_workload_8192(mode):
     print(f"[consumer] workload {w.name} {mode}", flush=True)
     p = Problem.from_workload(w).to_device()
     plan, D, Dc, rs, rm = run_consumer(p, mode=mode)
-    r = check_sampled(p, D, n_random=4096, seed=w.seed)
+    r = check_full(p, D, workload_reference(w, p))
+    print(f"[consumer] {w.name} {mode}: {r['n']} elements, {r['n_fail']} outside the bound, "
+          f"worst ratio {r['worst_ratio']:.4f}", flush=True)
+    assert r["n"] == w.M * w.N
     assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, r
     check_consumer_outputs(p, D, Dc, rs, rm)
     D2 = p.run(migemm.Plan(p.desc()))
