@@ -96,9 +96,8 @@ typedef enum migemm_status {
  *     (FP8_E4M3, FP8_E4M3, BF16, BF16);
  *   - each of A, B, C, D has exactly one unit stride, and its other stride
  *     is at least the extent of the contiguous dimension;
- *   - the non-unit stride times the element size is a multiple of 16 bytes;
- *   - if A is K-contiguous (a_cs == 1) or B is K-contiguous (b_rs == 1),
- *     K times the element size is a multiple of 16 bytes;
+ *   - the non-unit stride times the element size is a multiple of 16 bytes
+ *     (K itself may be anything, in every layout);
  *   - C and D have the same orientation (both row-major or both column-
  *     major); a column-major D is computed as D^T = B^T A^T;
  *   - the tile-consumer flag requires a row-major D;

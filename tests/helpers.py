@@ -71,6 +71,20 @@ class Problem:
             C = synth.random_matrix(gen, c_shape, BF16, "normal", K)
         return cls(M, N, K, A, B, C, a_rs, a_cs, b_rs, b_cs, alpha, beta, dtype, d_layout)
 
+    def poison_padding(self):
+        """Fill the storage past each operand row's last element (the padding
+        of the leading dimension) with NaN codes: a kernel that let any of it
+        reach an MFMA would give a non-finite D."""
+        nan = 0x7FC0 if self.dtype == BF16 else 0x7F
+        for t, rs, cs, rows, cols in ((self.A, self.a_rs, self.a_cs, self.M, self.K),
+                                      (self.B, self.b_rs, self.b_cs, self.K, self.N)):
+            v = t.view(torch.int16) if self.dtype == BF16 else t.view(torch.uint8)
+            if cs == 1:
+                v[:, cols:] = nan
+            else:
+                v[:, rows:] = nan
+        return self
+
     def desc(self, flags=0, max_workgroups=0, device=0):
         t = migemm.MIGEMM_BF16 if self.dtype == BF16 else migemm.MIGEMM_FP8_E4M3
         return migemm.make_desc(self.M, self.N, self.K, t, t, self.a_rs, self.a_cs, self.b_rs,

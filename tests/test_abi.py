@@ -117,7 +117,8 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(flags=migemm.MIGEMM_F_CONSUMER_OVERLAP | migemm.MIGEMM_F_TILE_CONSUMER |
           migemm.MIGEMM_F_STREAM_K_FORCE), migemm.MIGEMM_ERR_UNSUPPORTED),
     (dict(max_workgroups=-1), migemm.MIGEMM_ERR_INVALID_ARG),
-    (dict(K=5001, a_rs=5008), migemm.MIGEMM_ERR_MISALIGNED),                # K-contiguous A, K%8
+    (dict(K=5001, a_rs=5008), migemm.MIGEMM_OK),                            # K-contiguous A, any K
+    (dict(K=5001, a_rs=5001), migemm.MIGEMM_ERR_MISALIGNED),                # but 16-byte rows
 ])
 def test_validation_status_codes(over, status):
     assert migemm.gemm_desc_validate(desc_for(W, **over)) == status
@@ -137,12 +138,19 @@ def test_batch_validation(over, status):
     assert migemm.gemm_desc_validate(desc_for(W, **over)) == status
 
 
-def test_k_contiguity_rule_only_applies_to_k_contiguous_operands():
-    # A column-major (M-contiguous) and B row-major (N-contiguous): any K is fine
-    d = migemm.make_desc(64, 64, 17, 1, 1, 1, 64, 64, 1, 64, 1, 64, 1)
-    assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_OK
-    d = migemm.make_desc(64, 64, 17, 1, 1, 17, 1, 64, 1, 64, 1, 64, 1)      # A row-major
-    assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_ERR_MISALIGNED
+@pytest.mark.parametrize("t", [migemm.MIGEMM_BF16, migemm.MIGEMM_FP8_E4M3], ids=["bf16", "e4m3"])
+def test_any_k_in_every_layout(t):
+    """K needs no alignment in any layout; only the leading strides do."""
+    align = 8 if t == migemm.MIGEMM_BF16 else 16
+    for K in (1, 7, 9, 17, 5001):
+        ldk = -(-K // align) * align                   # K rounded up to 16 bytes
+        for a_rs, a_cs in ((ldk, 1), (1, 64)):         # A K- or M-contiguous
+            for b_rs, b_cs in ((64, 1), (1, ldk)):     # B N- or K-contiguous
+                d = migemm.make_desc(64, 64, K, t, t, a_rs, a_cs, b_rs, b_cs, 64, 1, 64, 1)
+                assert migemm.gemm_desc_validate(d) == migemm.MIGEMM_OK, (K, a_rs, b_rs)
+        d = migemm.make_desc(64, 64, K, t, t, K, 1, 64, 1, 64, 1, 64, 1)   # rows of K elements
+        want = migemm.MIGEMM_OK if K % align == 0 else migemm.MIGEMM_ERR_MISALIGNED
+        assert migemm.gemm_desc_validate(d) == want
 
 
 @pytest.mark.parametrize("t", [migemm.MIGEMM_BF16, migemm.MIGEMM_FP8_E4M3], ids=["bf16", "e4m3"])

@@ -80,6 +80,52 @@ def test_shapes_any_k_mn_contiguous(M, N, K):
     assert ok(check_full(p, D))
 
 
+K_TAIL_LAYOUTS = [("row", "col"), ("row", "row"), ("col", "col")]   # a K-contiguous operand
+
+
+@pytest.mark.parametrize("la,lb", K_TAIL_LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(64, 64, 1), (100, 130, 7), (257, 129, 9), (300, 260, 5001),
+                                   (520, 264, 71)])
+def test_any_k_with_k_contiguous_operands(la, lb, M, N, K):
+    """K not a multiple of 8: the last 16-byte chunk of a K-contiguous row
+    holds padding past K (NaN here), which the K loop must clear."""
+    g = torch.Generator().manual_seed(K * 131 + M)
+    p = Problem.random(g, M, N, K, la, lb, dist="normal").poison_padding().to_device()
+    print(f"[parity] any K {M}x{N}x{K} A {la} B {lb}", flush=True)
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    r = check_full(p, D)
+    assert ok(r), (la, lb, M, N, K, r)
+
+
+@pytest.mark.parametrize("la,lb", K_TAIL_LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(64, 64, 1), (130, 200, 15), (257, 129, 17), (300, 260, 1001)])
+def test_any_k_with_k_contiguous_operands_fp8(la, lb, M, N, K):
+    g = torch.Generator().manual_seed(K * 17 + N)
+    p = Problem.random(g, M, N, K, la, lb, dtype=synth.E4M3, alpha=0.0625).poison_padding()
+    p.to_device()
+    print(f"[parity] any K e4m3 {M}x{N}x{K} A {la} B {lb}", flush=True)
+    D = p.run(plan_for(p))
+    torch.cuda.synchronize()
+    r = check_full(p, D)
+    assert ok(r), (la, lb, M, N, K, r)
+
+
+def test_any_k_stream_k():
+    """The K tail in the last stream-K range of each tile."""
+    g = torch.Generator().manual_seed(5001)
+    p = Problem.random(g, 512, 512, 5001, "row", "col", dist="normal", alpha=0.5,
+                       beta=0.25).poison_padding().to_device()
+    plan = plan_for(p, flags=migemm.MIGEMM_F_STREAM_K_FORCE, max_workgroups=7)
+    assert plan.info.stream_k_tiles > 0
+    ws = torch.empty(max(plan.workspace_size, 256), dtype=torch.uint8, device="cuda")
+    migemm.gemm_workspace_init(plan.handle, ws)
+    D = p.new_d()
+    migemm.gemm_run(plan.handle, p.dA, p.dB, p.dC, D, p.alpha, p.beta, ws)
+    torch.cuda.synchronize()
+    assert ok(check_full(p, D))
+
+
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (257, 300, 192), (128, 384, 1040)])
 def test_shapes_fp8(la, lb, M, N, K):

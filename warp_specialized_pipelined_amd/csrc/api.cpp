@@ -99,9 +99,6 @@ int validate(const migemm_desc* d, Canon* out) {
   // 16-byte rows for every operand.
   if ((oa.ld * es) % 16 || (ob.ld * es) % 16 || (oc.ld * 2) % 16 || (od.ld * 2) % 16)
     return MIGEMM_ERR_MISALIGNED;
-  // A K-contiguous operand is fetched in 16-byte chunks along K.
-  const bool a_k = oa.row_major, b_k = !ob.row_major;
-  if ((a_k || b_k) && (d->K * es) % 16) return MIGEMM_ERR_MISALIGNED;
   // Batches: non-negative strides keeping every matrix 16-byte aligned; the
   // batches of D must not overlap (A, B and C may be shared).
   if (d->L < 0) return MIGEMM_ERR_INVALID_ARG;

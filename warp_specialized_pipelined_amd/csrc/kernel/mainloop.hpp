@@ -246,6 +246,34 @@ struct StageLoader {
     dma16(r, lds_at(slot + (wave * 8 + j) * 1024),
           (!MASK || kpos(j) < krem) ? off[j] : kOobOffset);
   }
+  // K-contiguous operands whose K is not a whole number of 16-byte chunks:
+  // the chunk that holds the last K elements of a row also holds whatever
+  // the row's storage has after K (padding, or anything else), which must
+  // not reach the MFMAs -- a NaN or infinity there times the other operand's
+  // zero is a NaN.  Once this wave's loads of the stage have landed (its own
+  // vmcnt), it clears the bytes at K index krem and beyond in the chunks it
+  // loaded; the barrier that follows publishes them.  Chunks wholly past K
+  // were loaded out of range (zeros) and whole ones are left as they are.
+  __device__ __forceinline__ void clear_k_tail(uint32_t slot, int krem, int wave, int lane) const {
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int nb = (krem - kpos(j)) * ES;  // valid bytes of this lane's chunk
+        if (nb > 0 && nb < 16) {
+          MIGEMM_LDS u32x4* p = (MIGEMM_LDS u32x4*)lds_at(slot + (wave * 8 + j) * 1024 + 16 * lane);
+          u32x4 x = *p;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int vb = nb - 4 * w;  // valid bytes of word w
+            x[w] &= vb >= 4 ? 0xFFFFFFFFu : (vb <= 0 ? 0u : (1u << (8 * vb)) - 1u);
+          }
+          *p = x;
+        }
+      }
+    } else {
+      (void)slot, (void)krem, (void)wave, (void)lane;
+    }
+  }
   __device__ __forceinline__ void load_all(int kt, uint32_t slot, int64_t K, int wave) const {
     int krem;
     const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt, K, &krem);
@@ -464,6 +492,20 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
 
   FW f;
   f.init(wm, wn, lane);
+  // The stage that the next barrier certifies (relative index rs, in the
+  // ring slot at `slot`) ends inside a 16-byte chunk of a K-contiguous
+  // operand: clear what lies past K (clear_k_tail).  Only the K tail can.
+  constexpr bool kAnyKMajor = AK || BK;
+  auto clear_tail = [&](int rs, uint32_t slot) {
+    if constexpr (kAnyKMajor) {
+      const int64_t krem = K - (int64_t)(k0 + rs) * G::kK;
+      if (krem > 0 && krem < G::kK && ((krem * ES) & 15) != 0) {
+        la.clear_k_tail(slot, (int)krem, wave, lane);
+        lb.clear_k_tail(slot + kB, (int)krem, wave, lane);
+        wait_lgkmcnt<0>();
+      }
+    }
+  };
   if (KT > 0) {
     // Prologue: stage 0 and stage 1 in flight (bf16: stage 1's B is loaded in
     // the first iteration), stage 0 certified, its k-step 0 read.
@@ -476,6 +518,7 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
       lb.load_all(k0 + 1, kStageBytes + kB, K, wave);
       wait_vmcnt<16>();
     }
+    clear_tail(0, 0);
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
@@ -512,6 +555,7 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     // reading stage d once its reads have returned.
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();
+    if constexpr (kMask) clear_tail(d + 1, nxt);
     barrier();
     // Anything the side work fetched after the previous barrier has landed.
     side.after_barrier(a, wave, lane);
