@@ -56,7 +56,9 @@ typedef enum migemm_status {
   MIGEMM_ERR_MISALIGNED = -3,  /* a base pointer or leading stride is not 16-byte aligned */
   MIGEMM_ERR_DEVICE = -4,      /* no HIP device, wrong ordinal, or not gfx950 */
   MIGEMM_ERR_LAUNCH = -5,      /* the HIP runtime rejected the kernel launch */
-  MIGEMM_ERR_TIMEOUT = -6      /* reserved: a bounded device-side wait expired */
+  MIGEMM_ERR_TIMEOUT = -6,     /* reserved: a bounded device-side wait expired */
+  MIGEMM_ERR_SCRATCH = -7      /* gemm_run_no_alloc: the plan needs more workspace than
+                                  MIGEMM_NO_ALLOC_SCRATCH_BYTES */
 } migemm_status;
 
 /* Plan flags. */
@@ -222,6 +224,26 @@ int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const vo
                                 const void* C, void* D, float alpha, float beta,
                                 float* row_sum, float* row_max, void* D_copy,
                                 void* workspace, void* stream);
+
+/* Size of the fixed device scratch of gemm_run_no_alloc: 64 MiB per device. */
+#define MIGEMM_NO_ALLOC_SCRATCH_BYTES (64ll << 20)
+
+/* gemm_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation with the same plan, but a plan that needs a workspace
+ * (stream-K) gets it from a fixed array inside the library instead of from
+ * the caller.  The array is MIGEMM_NO_ALLOC_SCRATCH_BYTES of device memory
+ * on every device the library runs on, held until the process ends; this
+ * call allocates and frees nothing.  A plan whose gemm_plan_workspace_size
+ * exceeds it gets MIGEMM_ERR_SCRATCH, with nothing launched (a stream-K plan
+ * fits with up to about 120 workgroups; cap it with max_workgroups).  Each
+ * call that uses the array first clears its arrival counters with a fill
+ * kernel on `stream`.  Every call on one device shares that device's array:
+ * calls whose executions overlap in time on one device race (use one stream,
+ * or order them), and the array keeps the last call's contents.  Arguments,
+ * results and the other errors are those of gemm_run. */
+int gemm_run_no_alloc(const migemm_plan* plan, const void* A, const void* B, const void* C,
+                      void* D, float alpha, float beta, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* gemm_status_string(int status);

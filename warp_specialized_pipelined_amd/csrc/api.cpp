@@ -328,9 +328,11 @@ int gemm_workspace_init(const migemm_plan* p, void* workspace, void* stream) {
   return e == hipSuccess ? MIGEMM_OK : MIGEMM_ERR_LAUNCH;
 }
 
-static int run_common(const migemm_plan* p, const void* A, const void* B, const void* C, void* D,
-                      float alpha, float beta, bool consumer, float* row_sum, float* row_max,
-                      void* D_copy, void* workspace, void* stream) {
+// Argument checks of a run, before anything is launched (the workspace is
+// checked by the caller: it is the caller's or the fixed scratch).
+static int check_run(const migemm_plan* p, const void* A, const void* B, const void* C,
+                     const void* D, float beta, bool consumer, const float* row_sum,
+                     const float* row_max, const void* D_copy) {
   if (!p) return MIGEMM_ERR_INVALID_ARG;
   if (consumer && !(p->desc.flags & MIGEMM_F_TILE_CONSUMER)) return MIGEMM_ERR_INVALID_ARG;
   if (p->M == 0 || p->N == 0) return MIGEMM_OK;
@@ -345,13 +347,14 @@ static int run_common(const migemm_plan* p, const void* A, const void* B, const 
       return MIGEMM_ERR_MISALIGNED;
     if (!(p->base.tiles_n > 0)) return MIGEMM_ERR_INVALID_ARG;
   }
-  if (p->workspace_bytes > 0) {
-    if (!workspace) return MIGEMM_ERR_INVALID_ARG;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
-  }
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return MIGEMM_ERR_DEVICE;
+  return MIGEMM_OK;
+}
 
+static int launch_run(const migemm_plan* p, const void* A, const void* B, const void* C, void* D,
+                      float alpha, float beta, bool consumer, float* row_sum, float* row_max,
+                      void* D_copy, void* workspace, hipStream_t stream) {
   KernelArgs a = p->base;
   // After a swap (column-major D) A and B trade places.
   a.A = p->swapped ? B : A;
@@ -369,8 +372,21 @@ static int run_common(const migemm_plan* p, const void* A, const void* B, const 
   }
   KernelSelect s = p->sel;
   s.consumer = consumer;
-  hipError_t e = migemm::launch_gemm(s, a, p->grid, static_cast<hipStream_t>(stream));
+  hipError_t e = migemm::launch_gemm(s, a, p->grid, stream);
   return e == hipSuccess ? MIGEMM_OK : MIGEMM_ERR_LAUNCH;
+}
+
+static int run_common(const migemm_plan* p, const void* A, const void* B, const void* C, void* D,
+                      float alpha, float beta, bool consumer, float* row_sum, float* row_max,
+                      void* D_copy, void* workspace, void* stream) {
+  int st = check_run(p, A, B, C, D, beta, consumer, row_sum, row_max, D_copy);
+  if (st != MIGEMM_OK || p->M == 0 || p->N == 0) return st;
+  if (p->workspace_bytes > 0) {
+    if (!workspace) return MIGEMM_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
+  }
+  return launch_run(p, A, B, C, D, alpha, beta, consumer, row_sum, row_max, D_copy, workspace,
+                    static_cast<hipStream_t>(stream));
 }
 
 int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* C, void* D,
@@ -386,6 +402,28 @@ int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const vo
                     stream);
 }
 
+static_assert(migemm::kNoAllocScratchBytes == MIGEMM_NO_ALLOC_SCRATCH_BYTES,
+              "the header states the fixed scratch size");
+
+int gemm_run_no_alloc(const migemm_plan* plan, const void* A, const void* B, const void* C,
+                      void* D, float alpha, float beta, void* stream) {
+  int st = check_run(plan, A, B, C, D, beta, false, nullptr, nullptr, nullptr);
+  if (st != MIGEMM_OK || plan->M == 0 || plan->N == 0) return st;
+  void* ws = nullptr;
+  if (plan->workspace_bytes > 0) {
+    if (plan->workspace_bytes > (size_t)MIGEMM_NO_ALLOC_SCRATCH_BYTES) return MIGEMM_ERR_SCRATCH;
+    if (migemm::no_alloc_scratch(plan->device, &ws) != hipSuccess) return MIGEMM_ERR_DEVICE;
+    // The arrival counters must start at zero; the array keeps whatever the
+    // last call on this device left, so they are cleared here every time
+    // (with a fill kernel, which a graph capture can record).
+    if (migemm::launch_zero_words(static_cast<uint32_t*>(ws), plan->sk_counters,
+                                  static_cast<hipStream_t>(stream)) != hipSuccess)
+      return MIGEMM_ERR_LAUNCH;
+  }
+  return launch_run(plan, A, B, C, D, alpha, beta, false, nullptr, nullptr, nullptr, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
 const char* gemm_status_string(int status) {
   switch (status) {
     case MIGEMM_OK: return "MIGEMM_OK";
@@ -395,6 +433,9 @@ const char* gemm_status_string(int status) {
     case MIGEMM_ERR_DEVICE: return "MIGEMM_ERR_DEVICE: no usable gfx950 device";
     case MIGEMM_ERR_LAUNCH: return "MIGEMM_ERR_LAUNCH: kernel launch failed";
     case MIGEMM_ERR_TIMEOUT: return "MIGEMM_ERR_TIMEOUT: device wait timed out";
+    case MIGEMM_ERR_SCRATCH:
+      return "MIGEMM_ERR_SCRATCH: the plan's workspace exceeds the fixed scratch of "
+             "gemm_run_no_alloc (MIGEMM_NO_ALLOC_SCRATCH_BYTES)";
     default: return "unknown migemm status";
   }
 }

@@ -8,6 +8,8 @@
 // hand-off ring to the consumer stage (handoff.hpp).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernel/epilogue.hpp"
 #include "kernel/gfx950.hpp"
 #include "kernel/handoff.hpp"
@@ -172,6 +174,30 @@ hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {
   blocks = blocks > 1024 ? 1024 : blocks;
   hipLaunchKernelGGL(zero_words, dim3(blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
+}
+
+// The device scratch of gemm_run_no_alloc: a stream-K workspace for callers
+// that cannot allocate device memory.  Each device holds its own copy from
+// the moment the code object is loaded there until the process ends.  In
+// host code the name is only a stand-in: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t no_alloc_scratch(int device, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[device] = ptr;
+  }
+  *out = addr[device];
+  return hipSuccess;
 }
 
 }  // namespace migemm

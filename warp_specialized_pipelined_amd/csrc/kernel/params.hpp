@@ -85,4 +85,8 @@ struct KernelArgs {
 constexpr int kSkPartialSlots = 2;
 constexpr int64_t kSkPartialBytes = (int64_t)kTileM * kTileN * 4;  // fp32 tile: 256 KiB
 
+// The fixed device scratch of the entry point that allocates nothing: room
+// for the stream-K workspace of a plan with up to about 120 workgroups.
+constexpr int64_t kNoAllocScratchBytes = 64ll << 20;
+
 }  // namespace migemm

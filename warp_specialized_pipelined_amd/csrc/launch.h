@@ -29,4 +29,8 @@ hipError_t launch_gemm(const KernelSelect& sel, const KernelArgs& args, int grid
 // Enqueue a kernel that sets n 32-bit words at p to zero.
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
+// The device address of the fixed scratch array (kNoAllocScratchBytes) on
+// `device`, which must be the current device.  Looked up once per device.
+hipError_t no_alloc_scratch(int device, void** out);
+
 }  // namespace migemm

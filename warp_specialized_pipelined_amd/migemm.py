@@ -24,6 +24,8 @@ MIGEMM_ERR_MISALIGNED = -3
 MIGEMM_ERR_DEVICE = -4
 MIGEMM_ERR_LAUNCH = -5
 MIGEMM_ERR_TIMEOUT = -6
+MIGEMM_ERR_SCRATCH = -7
+MIGEMM_NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 MIGEMM_F_TILE_CONSUMER = 0x1
 MIGEMM_F_STREAM_K = 0x2
@@ -35,7 +37,7 @@ MIGEMM_TILE_N = 256
 EXPORTED = [
     "gemm_desc_validate", "gemm_plan_create", "gemm_plan_destroy", "gemm_plan_get_info",
     "gemm_plan_workspace_size", "gemm_workspace_init", "gemm_run", "gemm_run_with_tile_consumer",
-    "gemm_status_string",
+    "gemm_run_no_alloc", "gemm_status_string",
 ]
 
 
@@ -106,6 +108,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_run_with_tile_consumer.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                                 vp, vp, vp, vp, vp]
     lib.gemm_run_with_tile_consumer.restype = i32
+    lib.gemm_run_no_alloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
+    lib.gemm_run_no_alloc.restype = i32
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -182,6 +186,15 @@ def gemm_run(plan, A, B, C, D, alpha: float, beta: float, workspace=None, stream
                          _ptr(workspace), _stream(stream))
     if check and st != MIGEMM_OK:
         raise MigemmError(st, "gemm_run")
+    return int(st)
+
+
+def gemm_run_no_alloc(plan, A, B, C, D, alpha: float, beta: float, stream=None,
+                      check: bool = True) -> int:
+    st = load().gemm_run_no_alloc(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha),
+                                  float(beta), _stream(stream))
+    if check and st != MIGEMM_OK:
+        raise MigemmError(st, "gemm_run_no_alloc")
     return int(st)
 
 
