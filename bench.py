@@ -83,7 +83,7 @@ def parse():
     ap.add_argument("--settle-seconds", type=float, default=1.5,
                     help="untimed back-to-back steps before the warm-up, for steady clocks")
     ap.add_argument("--variant", choices=["full", "consumer", "overlap", "plain", "fp8", "cfg1", "cfg2",
-                                          "cfg3", "copy"], default="full",
+                                          "cfg3", "copy", "trace"], default="full",
                     help="profiling runs: time one kernel only and print a short line "
                          "(copy = a plain 128 MiB device copy, the byte-counter calibration)")
     return ap.parse_args()
@@ -109,6 +109,9 @@ def run_variant(args):
         print(json.dumps({"variant": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
                           "ms": round(ms, 4), "GB/s": round(4 * n / (ms * 1e-3) / 1e9, 1)}))
         return
+    if args.variant == "trace":
+        run_trace(args)
+        return
     w = synth.WORKLOADS[VARIANTS[args.variant]]
     p = Problem.from_workload(w).to_device()
     D = p.new_d(0.0)
@@ -130,6 +133,41 @@ def run_variant(args):
     ms = time_calls(fn, args.steps, args.warmup, stream)
     print(json.dumps({"variant": args.variant, "workload": w.name, "ms": round(ms, 4),
                       "TFLOP/s": round(w.flops / (ms * 1e-3) / 1e12, 1)}))
+
+
+def run_trace(args):
+    """The 8192^3 tile-consumer workload with the hand-off debug trace, in
+    both schedules: a few untimed runs, then one traced run each, summarized
+    (where each tile's copy ran against the next tile's K loop, the ring's
+    occupancy, the waits)."""
+    import torch
+    from warp_specialized_pipelined_amd import handoff_trace, migemm, synth
+    from tests.helpers import Problem
+    w = synth.WORKLOADS[3]
+    p = Problem.from_workload(w).to_device()
+    D = p.new_d(0.0)
+    ld = (w.N + 255) // 256
+    rs = torch.empty((w.M, ld), dtype=torch.float32, device="cuda")
+    rm = torch.empty_like(rs)
+    Dc = torch.empty_like(D)
+    out = {"workload": w.name}
+    for name, extra in (("staged", 0), ("overlapped", migemm.MIGEMM_F_CONSUMER_OVERLAP)):
+        plan = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER | extra |
+                                  migemm.MIGEMM_F_HANDOFF_DEBUG))
+        ws = torch.empty(plan.workspace_size, dtype=torch.uint8, device="cuda")
+        run = lambda: migemm.gemm_run_with_tile_consumer(plan.handle, p.dA, p.dB, None, D, p.alpha,
+                                                         0.0, rs, rm, Dc, ws)
+        migemm.gemm_workspace_init(plan.handle, ws)
+        for _ in range(max(args.warmup, 1)):
+            run()
+        migemm.gemm_workspace_init(plan.handle, ws)
+        run()
+        st, info = migemm.gemm_debug_read(plan.handle, ws)
+        summ = handoff_trace.summarize(handoff_trace.records(ws, info), name)
+        summ["status"] = migemm.gemm_status_string(st)
+        summ["waits_given_up"] = int(info.waits_given_up)
+        out[name] = summ
+    print(json.dumps(out))
 
 
 def time_calls(fn, steps, warmup, stream):

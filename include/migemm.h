@@ -56,7 +56,7 @@ typedef enum migemm_status {
   MIGEMM_ERR_MISALIGNED = -3,  /* a base pointer or leading stride is not 16-byte aligned */
   MIGEMM_ERR_DEVICE = -4,      /* no HIP device, wrong ordinal, or not gfx950 */
   MIGEMM_ERR_LAUNCH = -5,      /* the HIP runtime rejected the kernel launch */
-  MIGEMM_ERR_TIMEOUT = -6,     /* reserved: a bounded device-side wait expired */
+  MIGEMM_ERR_TIMEOUT = -6,     /* a bounded hand-off wait expired (MIGEMM_F_HANDOFF_DEBUG) */
   MIGEMM_ERR_SCRATCH = -7      /* gemm_run_no_alloc: the plan needs more workspace than
                                   MIGEMM_NO_ALLOC_SCRATCH_BYTES */
 } migemm_status;
@@ -83,6 +83,19 @@ typedef enum migemm_status {
  * on its own (about 2.5% of the 8192^3 bf16 kernel's time).  It is the form
  * for consumer work that waits on long transfers rather than computing. */
 #define MIGEMM_F_CONSUMER_OVERLAP 0x8u
+/* With MIGEMM_F_TILE_CONSUMER (else INVALID_ARG): debugging of the hand-off
+ * ring.  gemm_plan_workspace_size then includes a debug area, which every
+ * run (gemm_run too) needs and gemm_workspace_init zeroes:
+ *   - each ring wait (acquire, wait) is bounded: after debug_wait_ticks of
+ *     the device's 100 MHz real-time clock (0: 10^8, one second) it gives
+ *     up, is counted, and the kernel goes on, so it always ends;
+ *     gemm_debug_read then reports MIGEMM_ERR_TIMEOUT (results may be wrong);
+ *   - every wave writes a trace record per tile of its workgroup: the clock
+ *     at each step of the protocol and the ring's occupancy at its commit
+ *     (migemm_debug_info describes the layout).
+ * debug_force_wait > 0 adds that much to every acquire's target: a wait
+ * that cannot pass, for testing the bounded wait itself. */
+#define MIGEMM_F_HANDOFF_DEBUG 0x10u
 
 /* Output tile of the persistent scheduler (and the hand-off unit). */
 #define MIGEMM_TILE_M 256
@@ -128,6 +141,9 @@ typedef struct migemm_desc {
   int32_t reserved;                       /* must be 0 */
   int64_t L;                              /* batch count (0 or 1: one product) */
   int64_t a_bs, b_bs, c_bs, d_bs;         /* batch strides in elements (L > 1) */
+  int64_t debug_wait_ticks;               /* MIGEMM_F_HANDOFF_DEBUG: wait budget (0: default) */
+  int32_t debug_force_wait;               /* MIGEMM_F_HANDOFF_DEBUG: see there; else 0 */
+  int32_t reserved2;                      /* must be 0 */
 } migemm_desc;
 
 /* What a plan chose (for tracing and tests). */
@@ -224,6 +240,35 @@ int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const vo
                                 const void* C, void* D, float alpha, float beta,
                                 float* row_sum, float* row_max, void* D_copy,
                                 void* workspace, void* stream);
+
+/* What the hand-off debug area of a MIGEMM_F_HANDOFF_DEBUG plan holds.  The
+ * trace starts trace_offset bytes into the workspace: for workgroup g
+ * (0 .. grid-1), wave w (0 .. waves-1) and the workgroup's n-th tile (0 ..
+ * trace_tiles-1), a record of trace_words uint64 at index
+ * ((g * waves + w) * trace_tiles + n) * trace_words, holding the device
+ * real-time clock (100 MHz) when the wave
+ *   [0] began the tile's K loop, [1] ended it, [2] acquired the tile's ring
+ *   slot, [3] committed the tile, [4] saw it committed by every wave (its
+ *   consumer's wait), [5] stored the tile's first and [6] its last copy
+ *   step, [7] released the slot,
+ * then [8] the ring's occupancy right after this wave's commit (tiles
+ * committed by every wave minus tiles released by every wave, over both
+ * slots) and [9] the tile id (records of tiles a workgroup does not have
+ * stay zero). */
+typedef struct migemm_debug_info {
+  uint32_t waits_given_up;     /* bounded waits that expired since the last init */
+  uint32_t max_occupancy;      /* largest ring occupancy seen, in tiles */
+  int64_t trace_offset;        /* bytes from the workspace to the first record */
+  int32_t grid, waves, trace_tiles, trace_words;
+} migemm_debug_info;
+
+/* Synchronizes `stream`, then reads the debug header of a
+ * MIGEMM_F_HANDOFF_DEBUG plan's workspace into *out.  Returns
+ * MIGEMM_ERR_TIMEOUT if a bounded ring wait has given up since the last
+ * gemm_workspace_init, else MIGEMM_OK (or INVALID_ARG for a plan without
+ * the flag, a NULL argument; DEVICE if the copy fails). */
+int gemm_debug_read(const migemm_plan* plan, const void* workspace, void* stream,
+                    migemm_debug_info* out);
 
 /* Size of the fixed device scratch of gemm_run_no_alloc: 64 MiB per device. */
 #define MIGEMM_NO_ALLOC_SCRATCH_BYTES (64ll << 20)

@@ -85,11 +85,11 @@ class Problem:
                 v[:, rows:] = nan
         return self
 
-    def desc(self, flags=0, max_workgroups=0, device=0):
+    def desc(self, flags=0, max_workgroups=0, device=0, **extra):
         t = migemm.MIGEMM_BF16 if self.dtype == BF16 else migemm.MIGEMM_FP8_E4M3
         return migemm.make_desc(self.M, self.N, self.K, t, t, self.a_rs, self.a_cs, self.b_rs,
                                 self.b_cs, self.c_rs, self.c_cs, self.d_rs, self.d_cs, device=device,
-                                flags=flags, max_workgroups=max_workgroups)
+                                flags=flags, max_workgroups=max_workgroups, **extra)
 
     # ---------------------------------------------------------------- GPU
     def to_device(self, device="cuda"):

@@ -51,6 +51,11 @@ int main(void) {
   printf("sizeof.info %zu\n", sizeof(migemm_plan_info));
   F(migemm_desc, M); F(migemm_desc, a_type); F(migemm_desc, a_rs); F(migemm_desc, d_cs);
   F(migemm_desc, device); F(migemm_desc, flags); F(migemm_desc, max_workgroups);
+  F(migemm_desc, L); F(migemm_desc, d_bs); F(migemm_desc, debug_wait_ticks);
+  F(migemm_desc, debug_force_wait); F(migemm_desc, reserved2);
+  printf("sizeof.dbg %zu\n", sizeof(migemm_debug_info));
+  F(migemm_debug_info, max_occupancy); F(migemm_debug_info, trace_offset);
+  F(migemm_debug_info, trace_words);
   F(migemm_plan_info, grid); F(migemm_plan_info, tile_k); F(migemm_plan_info, handoff_slots);
   return 0;
 }
@@ -64,11 +69,14 @@ int main(void) {
     import ctypes
     assert int(got["sizeof.desc"]) == ctypes.sizeof(migemm.migemm_desc)
     assert int(got["sizeof.info"]) == ctypes.sizeof(migemm.migemm_plan_info)
+    assert int(got["sizeof.dbg"]) == ctypes.sizeof(migemm.migemm_debug_info)
+    classes = {"migemm_desc": migemm.migemm_desc, "migemm_plan_info": migemm.migemm_plan_info,
+               "migemm_debug_info": migemm.migemm_debug_info}
     for key, v in got.items():
         if key.startswith("sizeof"):
             continue
         s, f = key.split(".")
-        cls = migemm.migemm_desc if s == "migemm_desc" else migemm.migemm_plan_info
+        cls = classes[s]
         assert getattr(cls, f).offset == int(v), key
 
 
@@ -117,6 +125,13 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(flags=migemm.MIGEMM_F_CONSUMER_OVERLAP | migemm.MIGEMM_F_TILE_CONSUMER |
           migemm.MIGEMM_F_STREAM_K_FORCE), migemm.MIGEMM_ERR_UNSUPPORTED),
     (dict(max_workgroups=-1), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=migemm.MIGEMM_F_HANDOFF_DEBUG), migemm.MIGEMM_ERR_INVALID_ARG),      # no consumer
+    (dict(flags=migemm.MIGEMM_F_HANDOFF_DEBUG | migemm.MIGEMM_F_TILE_CONSUMER), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_HANDOFF_DEBUG | migemm.MIGEMM_F_TILE_CONSUMER,
+          debug_wait_ticks=1000, debug_force_wait=1), migemm.MIGEMM_OK),
+    (dict(debug_wait_ticks=1000), migemm.MIGEMM_ERR_INVALID_ARG),                   # needs the flag
+    (dict(flags=migemm.MIGEMM_F_HANDOFF_DEBUG | migemm.MIGEMM_F_TILE_CONSUMER,
+          debug_force_wait=-1), migemm.MIGEMM_ERR_INVALID_ARG),
     (dict(K=5001, a_rs=5008), migemm.MIGEMM_OK),                            # K-contiguous A, any K
     (dict(K=5001, a_rs=5001), migemm.MIGEMM_ERR_MISALIGNED),                # but 16-byte rows
 ])

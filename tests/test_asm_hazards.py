@@ -107,3 +107,34 @@ def test_checker_sees_the_hazard():
     # the non-temporal form is checked the same way
     nt = [x.replace("offen lds", "offen nt lds") for x in lines]
     assert LDS_LOAD.match(nt[3]) and check_load(nt, 3)
+
+
+def _innermost_k_loops(lines):
+    """(first, last) line of every innermost loop that holds MFMAs: the K
+    loops (a back-edge branch to an earlier label closes a loop)."""
+    labels = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(\.LBB\w+):", l)
+        if m:
+            labels[m.group(1)] = i
+    loops = []
+    for i, l in enumerate(lines):
+        m = re.search(r"s_c?branch\w*\s+(\.LBB\w+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            loops.append((labels[m.group(1)], i))
+    inner = [(a, b) for a, b in loops
+             if not any(a <= c and d <= b and (c, d) != (a, b) for c, d in loops)]
+    return [(a, b) for a, b in inner if sum("v_mfma" in x for x in lines[a:b]) >= 16]
+
+
+def test_no_scratch_access_inside_a_k_loop(kernels):
+    """A scratch reload inside a K loop waits (vmcnt) for every stage load in
+    flight, which stalls the ring; spills may only sit in per-tile code."""
+    bad = {}
+    for name, lines in kernels.items():
+        loops = _innermost_k_loops(lines)
+        assert loops, f"no K loop found in {name}"
+        hits = [i for a, b in loops for i in range(a, b) if "scratch_" in lines[i]]
+        if hits:
+            bad[name] = [lines[i].strip() for i in hits[:3]]
+    assert not bad, bad

@@ -28,6 +28,9 @@ struct migemm_plan {
   int64_t sk_counters;        // 32-bit counters
   size_t sk_counter_bytes;    // rounded up to 256 bytes
   size_t workspace_bytes;
+  // Hand-off debug area (MIGEMM_F_HANDOFF_DEBUG): header, then trace records.
+  bool debug;
+  int trace_tiles;
 };
 
 namespace {
@@ -75,10 +78,16 @@ struct Canon {
 
 int validate(const migemm_desc* d, Canon* out) {
   if (!d) return MIGEMM_ERR_INVALID_ARG;
-  if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0)
+  if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0 ||
+      d->reserved2 != 0 || d->debug_wait_ticks < 0 || d->debug_force_wait < 0)
     return MIGEMM_ERR_INVALID_ARG;
   constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
-  if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | kStreamK)) != 0)
+  if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | MIGEMM_F_HANDOFF_DEBUG |
+                    kStreamK)) != 0)
+    return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & MIGEMM_F_HANDOFF_DEBUG) && !(d->flags & MIGEMM_F_TILE_CONSUMER))
+    return MIGEMM_ERR_INVALID_ARG;
+  if (!(d->flags & MIGEMM_F_HANDOFF_DEBUG) && (d->debug_wait_ticks != 0 || d->debug_force_wait != 0))
     return MIGEMM_ERR_INVALID_ARG;
   if ((d->flags & MIGEMM_F_CONSUMER_OVERLAP) && !(d->flags & MIGEMM_F_TILE_CONSUMER))
     return MIGEMM_ERR_INVALID_ARG;
@@ -155,6 +164,10 @@ int validate(const migemm_desc* d, Canon* out) {
 // 4000x3000x5000, 8192x1024x8192 and 2048x2048x8192 bf16).  When the units
 // fall on tile boundaries nothing is split and whole tiles are the same.
 constexpr int64_t kSkFixupStages = 24;
+
+// Default budget of a bounded hand-off wait: 10^8 ticks of the 100 MHz
+// real-time clock, one second.
+constexpr int64_t kDefaultWaitTicks = 100000000;
 
 bool stream_k_pays(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
   const int64_t units = (T - sk_first) * kt;
@@ -257,6 +270,13 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
     grid = a.num_tiles;
   }
   p->grid = grid;
+  if (desc->flags & MIGEMM_F_HANDOFF_DEBUG) {
+    p->debug = true;
+    p->trace_tiles = grid > 0 ? (a.num_tiles + grid - 1) / grid : 0;
+    p->workspace_bytes = (size_t)migemm::kDebugHeaderBytes +
+                         (size_t)grid * migemm::kWaves * (size_t)p->trace_tiles *
+                             migemm::kTraceWords * sizeof(uint64_t);
+  }
 
   hipError_t e = migemm::prepare_kernel(p->sel);
   if (e == hipSuccess && (desc->flags & MIGEMM_F_TILE_CONSUMER)) {
@@ -323,7 +343,9 @@ int gemm_workspace_init(const migemm_plan* p, void* workspace, void* stream) {
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != p->device) return MIGEMM_ERR_DEVICE;
-  hipError_t e = migemm::launch_zero_words(static_cast<uint32_t*>(workspace), p->sk_counters,
+  // Stream-K: the arrival counters; debug: the header and every record.
+  const int64_t words = p->debug ? (int64_t)(p->workspace_bytes / 4) : p->sk_counters;
+  hipError_t e = migemm::launch_zero_words(static_cast<uint32_t*>(workspace), words,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIGEMM_OK : MIGEMM_ERR_LAUNCH;
 }
@@ -370,6 +392,14 @@ static int launch_run(const migemm_plan* p, const void* A, const void* B, const 
     a.sk_arrivals = static_cast<uint32_t*>(workspace);
     a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->sk_counter_bytes);
   }
+  if (p->debug && consumer) {
+    a.dbg = static_cast<uint32_t*>(workspace);
+    a.trace = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) +
+                                          migemm::kDebugHeaderBytes);
+    a.spin_budget = p->desc.debug_wait_ticks > 0 ? p->desc.debug_wait_ticks : kDefaultWaitTicks;
+    a.force_wait = p->desc.debug_force_wait;
+    a.trace_tiles = p->trace_tiles;
+  }
   KernelSelect s = p->sel;
   s.consumer = consumer;
   hipError_t e = migemm::launch_gemm(s, a, p->grid, stream);
@@ -400,6 +430,24 @@ int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const vo
                                 float* row_max, void* D_copy, void* workspace, void* stream) {
   return run_common(plan, A, B, C, D, alpha, beta, true, row_sum, row_max, D_copy, workspace,
                     stream);
+}
+
+int gemm_debug_read(const migemm_plan* p, const void* workspace, void* stream,
+                    migemm_debug_info* out) {
+  if (!p || !out || !workspace || !p->debug) return MIGEMM_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  uint32_t head[2] = {0, 0};
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||
+      hipMemcpy(head, workspace, sizeof(head), hipMemcpyDeviceToHost) != hipSuccess)
+    return MIGEMM_ERR_DEVICE;
+  out->waits_given_up = head[0];
+  out->max_occupancy = head[1];
+  out->trace_offset = migemm::kDebugHeaderBytes;
+  out->grid = p->grid;
+  out->waves = migemm::kWaves;
+  out->trace_tiles = p->trace_tiles;
+  out->trace_words = migemm::kTraceWords;
+  return head[0] > 0 ? MIGEMM_ERR_TIMEOUT : MIGEMM_OK;
 }
 
 static_assert(migemm::kNoAllocScratchBytes == MIGEMM_NO_ALLOC_SCRATCH_BYTES,

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     // stage on its 64 rows of the tile as the epilogue left it staged in
     // LDS, and releases the slot before the next K loop refills the ring
     // over the staging area.
-    HandoffRing::init();
+    HandoffRing::init(a);
     __syncthreads();
     TileConsumer cons;
     cons.idle();
@@ -81,14 +81,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
       const TileCoord t = tile_of(L, a);
       const KernelArgs ab = batch_args(a, t.l);
+      trace_event(n, wave, kEvLoopBegin, lane);
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
+      trace_event(n, wave, kEvLoopEnd, lane);
       const int s = n % kHandoffSlots;
-      HandoffRing::acquire(s, n / kHandoffSlots);
+      HandoffRing::acquire(s, n / kHandoffSlots, lane);
+      trace_event(n, wave, kEvAcquired, lane);
       const LaneIds ie(lane, wave);
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
-      HandoffRing::commit(s, L, wave, lane);
-      cons.begin(a, s, n / kHandoffSlots, wave, lane);
+      const uint32_t occ = HandoffRing::commit(s, L, wave, lane);
+      uint64_t* rec = trace_record(n, wave);
+      trace_put(rec, kEvCommitted, now_ticks(), lane);
+      trace_put(rec, kTrOccupancy, occ, lane);
+      trace_put(rec, kTrTileId, (uint64_t)L, lane);
+      cons.begin(a, s, n / kHandoffSlots, n, wave, lane);
       cons.fold_staged(wave, lane);
       cons.copy_staged(wave, lane);
       wait_lgkmcnt<0>();  // staging reads done ...
@@ -98,9 +105,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     // Overlapped schedule.  Tile n of this workgroup goes through hand-off
     // slot n % S (use n / S).  Its row statistics are folded right after its
     // commit, from the staged tile; its copy runs inside tile n+1's K loop,
-    // fetching the tile back from D (the last tile's from its staging, after
-    // the loop).
-    HandoffRing::init();
+    // fetching the tile back from D, and whatever the loop leaves, plus the
+    // release of its slot, comes after tile n+1's commit: the ring then
+    // holds two committed tiles.  The last tile is copied from its staging
+    // area after the loop.
+    HandoffRing::init(a);
     __syncthreads();
     TileConsumer cons;
     cons.idle();
@@ -108,15 +117,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
     for (int L = first; L < a.num_tiles; L += gridDim.x, ++n) {
       const TileCoord t = tile_of(L, a);
       const KernelArgs ab = batch_args(a, t.l);
+      trace_event(n, wave, kEvLoopBegin, lane);
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, cons);
-      cons.drain(a, wave, lane);
+      trace_event(n, wave, kEvLoopEnd, lane);
       const int s = n % kHandoffSlots;
-      HandoffRing::acquire(s, n / kHandoffSlots);
+      HandoffRing::acquire(s, n / kHandoffSlots, lane);
+      trace_event(n, wave, kEvAcquired, lane);
       const LaneIds ie(lane, wave);
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
-      HandoffRing::commit(s, L, wave, lane);
-      cons.begin(a, s, n / kHandoffSlots, wave, lane);
+      const uint32_t occ = HandoffRing::commit(s, L, wave, lane);
+      uint64_t* rec = trace_record(n, wave);
+      trace_put(rec, kEvCommitted, now_ticks(), lane);
+      trace_put(rec, kTrOccupancy, occ, lane);
+      trace_put(rec, kTrTileId, (uint64_t)L, lane);
+      cons.drain(wave, lane);  // tile n-1: steps the K loop left, and its release
+      cons.begin(a, s, n / kHandoffSlots, n, wave, lane);
       cons.fold_staged(wave, lane);
       wait_lgkmcnt<0>();
       barrier();

@@ -25,14 +25,25 @@
 // wave folds the row statistics from the tile as the epilogue left it
 // staged in LDS (fold_staged), before the next K loop refills the ring over
 // the staging area.  The copy runs on one of two schedules:
-//   staged (default): at once, from the staged tile (copy_staged);
+//   staged (default): at once, from the staged tile (copy_staged), and the
+//     slot is released right after;
 //   overlapped: inside tile n+1's K loop, one step per iteration fetched
-//     back from D (after_barrier, drain); the last tile's from its staging.
+//     back from D (after_barrier); steps the loop did not reach are finished
+//     after tile n+1's commit (drain), and tile n's slot is released there
+//     too -- so when tile n+1 is committed the ring holds two committed
+//     tiles, n and n+1, and the producer never waits for the consumer's last
+//     steps of tile n.  The last tile is copied from its staging area.
 // The overlap is what the hand-off ring is for when consumer work waits on
 // memory or links; for this consumer stage the staged schedule costs less:
 // the K loop's side work holds the MFMA waves longer than the work takes on
 // its own.
 //
+// Debugging (kernel arguments dbg/trace, set by the plan's hand-off debug
+// flag): every ring wait is bounded by a budget of s_memrealtime ticks and
+// counts a wait that gave up in the workspace header (the kernel then goes
+// on, so it always ends), and each wave writes one trace record per tile of
+// its workgroup: the real-time clock at the events below, the ring's
+// occupancy right after its commit, and the tile id.
 // Consumer work for a 256 x 256 tile at tile column t: for each of its rows r,
 // over the tile's columns below N, with x_j the bf16 value of D[r][256t + j]
 // widened to fp32:
@@ -54,39 +65,143 @@ namespace migemm {
 
 typedef MIGEMM_LDS uint32_t lds_u32;
 
+// Trace record of one wave and tile (kTraceWords 64-bit words): the
+// real-time clock (100 MHz) when the wave began the tile's K loop, ended it,
+// acquired the tile's slot, committed the tile, saw the tile committed by
+// all waves (its consumer's wait), stored the tile's first and last copy
+// step, and released the slot; then the ring occupancy right after this
+// wave's commit (tiles committed by every wave minus tiles released by every
+// wave, over both slots) and the tile id.
+enum TraceWord {
+  kEvLoopBegin = 0, kEvLoopEnd, kEvAcquired, kEvCommitted, kEvWaitDone, kEvCopyFirst, kEvCopyLast,
+  kEvReleased, kTrOccupancy, kTrTileId
+};
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// The debug settings, copied into LDS once per kernel (HandoffRing::init)
+// and read back where they are used, so that none of them occupies a
+// register across the K loops.
+struct HandoffDebug {
+  uint32_t* dbg;         // debug header, or NULL: unbounded waits, no trace
+  uint64_t* trace;       // trace records, or NULL
+  int64_t budget;        // ticks a bounded wait may spin
+  uint32_t force;        // added to every acquire's target (a wait that cannot pass)
+  int32_t trace_tiles;   // records per wave
+};
+static_assert(sizeof(HandoffDebug) <= kHandoffRecOffset - kHandoffDebugOffset, "debug block");
+
+// The block is kept as 64-bit words: [0] dbg, [1] trace, [2] budget,
+// [3] force | trace_tiles << 32; then one record pointer per wave.
+__device__ __forceinline__ MIGEMM_LDS uint64_t* debug_words() {
+  return (MIGEMM_LDS uint64_t*)lds_at(kHandoffDebugOffset);
+}
+__device__ __forceinline__ HandoffDebug handoff_debug() {
+  const MIGEMM_LDS uint64_t* q = debug_words();
+  HandoffDebug d;
+  d.dbg = reinterpret_cast<uint32_t*>(q[0]);
+  d.trace = reinterpret_cast<uint64_t*>(q[1]);
+  d.budget = (int64_t)q[2];
+  d.force = (uint32_t)q[3];
+  d.trace_tiles = (int32_t)(q[3] >> 32);
+  return d;
+}
+__device__ __forceinline__ MIGEMM_LDS uint64_t* rec_slot(int wave) {
+  return (MIGEMM_LDS uint64_t*)lds_at(kHandoffRecOffset + 8 * wave);
+}
+__device__ __forceinline__ uint64_t* rec_of(int wave) {
+  return reinterpret_cast<uint64_t*>(*rec_slot(wave));
+}
+
+// The trace record of this wave for the workgroup's seq-th tile, or NULL.
+__device__ __forceinline__ uint64_t* trace_record(int seq, int wave) {
+  const HandoffDebug d = handoff_debug();
+  if (d.trace == nullptr) return nullptr;
+  return d.trace + ((int64_t)(blockIdx.x * kWaves + wave) * d.trace_tiles + seq) * kTraceWords;
+}
+// One word of a record, written by lane 0 with a vector store.
+__device__ __forceinline__ void trace_put(uint64_t* rec, int word, uint64_t v, int lane) {
+  if (rec != nullptr && lane == 0) rec[word] = v;
+}
+// The real-time clock into a word of this wave's record of the workgroup's
+// seq-th tile (looked up here).
+__device__ __forceinline__ void trace_event(int seq, int wave, int word, int lane) {
+  trace_put(trace_record(seq, wave), word, now_ticks(), lane);
+}
+
 struct HandoffRing {
   enum { kTileId = 0, kFull = 1, kEmpty = 2 };
   __device__ __forceinline__ static lds_u32* word(int slot, int field) {
     return (lds_u32*)lds_at(kHandoffOffset + slot * 16 + field * 4);
   }
-  // All slots empty and unused; call before the kernel's first barrier.
-  __device__ __forceinline__ static void init() {
+  // All slots empty and unused, and the debug settings in place; call
+  // before the kernel's first barrier.
+  __device__ __forceinline__ static void init(const KernelArgs& a) {
     if (threadIdx.x < kHandoffSlots * 4) *word(threadIdx.x >> 2, threadIdx.x & 3) = 0;
+    if (threadIdx.x == 0) {
+      MIGEMM_LDS uint64_t* q = debug_words();
+      q[0] = reinterpret_cast<uint64_t>(a.dbg);
+      q[1] = reinterpret_cast<uint64_t>(a.trace);
+      q[2] = (uint64_t)a.spin_budget;
+      q[3] = (uint64_t)(uint32_t)a.force_wait | ((uint64_t)(uint32_t)a.trace_tiles << 32);
+    }
+    if (threadIdx.x < kWaves) *rec_slot(threadIdx.x) = 0;
   }
-  __device__ __forceinline__ static void spin_until(lds_u32* p, uint32_t target) {
-    while (__atomic_load_n(p, __ATOMIC_RELAXED) < target) __builtin_amdgcn_s_sleep(1);
+  __device__ __forceinline__ static uint32_t load(lds_u32* p) {
+    return __atomic_load_n(p, __ATOMIC_RELAXED);
+  }
+  // Spin until *p >= target.  With a debug header the spin is bounded: after
+  // the budget's ticks the wait gives up, is counted in the header, and the
+  // caller goes on (so the kernel always ends).
+  __device__ __forceinline__ static void spin_until(lds_u32* p, uint32_t target, int lane) {
+    if (load(p) >= target) return;
+    const HandoffDebug d = handoff_debug();
+    if (d.dbg == nullptr) {
+      while (load(p) < target) __builtin_amdgcn_s_sleep(1);
+      return;
+    }
+    const uint64_t t0 = now_ticks();
+    while (load(p) < target) {
+      if ((int64_t)(now_ticks() - t0) > d.budget) {
+        if (lane == 0) __hip_atomic_fetch_add(d.dbg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
   // Producer side.
-  __device__ __forceinline__ static void acquire(int slot, uint32_t use) {
-    spin_until(word(slot, kEmpty), use * kWaves);
+  __device__ __forceinline__ static void acquire(int slot, uint32_t use, int lane) {
+    spin_until(word(slot, kEmpty), use * kWaves + handoff_debug().force, lane);
   }
   // Publishes the caller's stores of the tile: the workgroup-scope release
   // fence orders them before the count.  (The waves of a workgroup share
   // the compute unit's path to memory, so outside tgsplit mode this fence
   // compiles to no wait at all: the stores may still be in flight.)
-  __device__ __forceinline__ static void commit(int slot, int tile_id, int wave, int lane) {
+  // With a debug header, returns the ring's occupancy right after this
+  // commit -- the tiles all waves have committed minus the tiles all waves
+  // have released, over both slots -- and keeps the largest in the header;
+  // else 0.
+  __device__ __forceinline__ static uint32_t commit(int slot, int tile_id, int wave, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) {
       if (wave == 0) __atomic_store_n(word(slot, kTileId), (uint32_t)tile_id, __ATOMIC_RELAXED);
       __atomic_fetch_add(word(slot, kFull), 1u, __ATOMIC_RELAXED);
     }
+    uint32_t* dbg = handoff_debug().dbg;
+    if (dbg == nullptr) return 0;
+    uint32_t occ = 0;
+#pragma unroll
+    for (int s = 0; s < kHandoffSlots; ++s)
+      occ += load(word(s, kFull)) / kWaves - load(word(s, kEmpty)) / kWaves;
+    if (lane == 0) __hip_atomic_fetch_max(dbg + 1, occ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return occ;
   }
   // Consumer side.  Returns the committed tile's id; the acquire fence keeps
   // the consumer's reads of the tile after the observed commit.
-  __device__ __forceinline__ static int wait(int slot, uint32_t use) {
-    spin_until(word(slot, kFull), (use + 1) * kWaves);
+  __device__ __forceinline__ static int wait(int slot, uint32_t use, int lane) {
+    spin_until(word(slot, kFull), (use + 1) * kWaves, lane);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return (int)__atomic_load_n(word(slot, kTileId), __ATOMIC_RELAXED);
+    return (int)load(word(slot, kTileId));
   }
   // The slot (its tile id) is free again.  The consumer's reads of the tile
   // have completed by then (its last fetch was waited for and read back just
@@ -156,11 +271,12 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 //   iteration i+2: after its barrier, store the copy.
 // Going through LDS keeps every wait explicit: the compiler never sees an
 // outstanding load, so it never answers one with a vmcnt(0) that would also
-// drain the ring.  Steps the K loop did not reach are finished after it
-// (drain): the ring and the wave's staging area are idle until the wave's
-// epilogue, so the remaining fetches all go out at once into the staging
-// area and the drain waits for memory once.  The workgroup's last tile has
-// no K loop after it and is copied from its staging area.
+// drain the ring.  Steps the K loop did not reach are finished after the
+// next tile's commit (drain), kConsumerDepth at a time through the landing
+// slots (the staging area then holds the next tile, which its row
+// statistics still need); the drain also releases the slot.  The
+// workgroup's last tile has no K loop after it and is copied from its
+// staging area.
 struct TileConsumer {
   static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
   // Buffer resources from the tile's origin: D (fetch) and D_copy (store)
@@ -178,12 +294,14 @@ struct TileConsumer {
   int read;                     // copy steps read back so far
   int slot;
   bool active;                  // copy steps of this tile remain to be stored
+  bool finished;                // all steps stored; the slot waits for its release (overlapped)
   bool pending;                 // step pend_j is read back and waits for its store
   int pend_j;
   u32x4 v;                      // the pending step's 16 bytes
 
   __device__ __forceinline__ void idle() {
     active = false;
+    finished = false;
     pending = false;
   }
 
@@ -191,23 +309,20 @@ struct TileConsumer {
     static_assert((kConsumerDepth & (kConsumerDepth - 1)) == 0, "landing slots are indexed with a mask");
     return kConsumerSlotOffset + (wave * kConsumerDepth + (c & (kConsumerDepth - 1))) * kConsumerSlotBytes;
   }
-  // Where the drain lands step j: the wave's own epilogue staging area.
-  __device__ __forceinline__ static uint32_t drain_slot(int wave, int j) {
-    static_assert(kSteps * kConsumerSlotBytes <= kStagingWaveBytes,
-                  "a wave's remaining steps must fit in its staging area");
-    return wave * kStagingWaveBytes + j * kConsumerSlotBytes;
-  }
-
-  // Wait for the use-th commit of `slot`, then set up this lane's share.
-  __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int wave,
-                                        int lane) {
+  // Wait for the use-th commit of `slot` (the workgroup's seq-th tile), then
+  // set up this lane's share.
+  __device__ __forceinline__ void begin(const KernelArgs& a, int slot_, uint32_t use, int seq,
+                                        int wave, int lane) {
     // The lane id as a value the compiler cannot see through: the per-lane
     // offsets below are then computed here, per tile, instead of once at the
     // kernel's start and kept across the K loops in scratch (each reload a
     // round trip to memory that waits behind every load in flight).
     asm volatile("" : "+v"(lane));
     slot = slot_;
-    const int tile_id = uni(HandoffRing::wait(slot, use));
+    const int tile_id = uni(HandoffRing::wait(slot, use, lane));
+    uint64_t* rec = trace_record(seq, wave);
+    trace_put(rec, kEvWaitDone, now_ticks(), lane);
+    if (lane == 0) *rec_slot(wave) = reinterpret_cast<uint64_t>(rec);
     const TileCoord t = tile_of(tile_id, a);
     const KernelArgs ab = batch_args(a, t.l);
     const int64_t r0 = (int64_t)t.tm * kTileM;
@@ -330,15 +445,21 @@ struct TileConsumer {
     }
   }
 
-  // The tile's last copy step is stored: the slot is free again.  The
-  // tile's reads all completed before their values were stored.
-  __device__ __forceinline__ void done(int lane) {
-    active = false;
+  // A trace event of the tile this wave's consumer works on.
+  __device__ __forceinline__ static void cons_trace(int word, int wave, int lane) {
+    trace_put(rec_of(wave), word, now_ticks(), lane);
+  }
+
+  // Releases the tile's slot.  The tile's reads all completed before their
+  // values were stored.
+  __device__ __forceinline__ void release(int wave, int lane) {
+    finished = false;
+    cons_trace(kEvReleased, wave, lane);
     HandoffRing::release(slot, lane);
   }
 
-  // Staged schedule: the copy steps kCopyBatch at a time from the staged
-  // tile, then the release.
+  // Staged schedule (and the overlapped one's last tile): the copy steps
+  // kCopyBatch at a time from the staged tile, then the release.
   static constexpr int kCopyBatch = 8;
   __device__ __forceinline__ void copy_staged(int wave, int lane) {
     static_assert(kSteps % kCopyBatch == 0, "whole batches of steps");
@@ -351,9 +472,12 @@ struct TileConsumer {
         x[q] = *(const MIGEMM_LDS u32x4*)lds_at(staged_at(wave, lane, j0 + q));
 #pragma unroll
       for (int q = 0; q < kCopyBatch; ++q) store_copy(x[q], j0 + q, lane);
+      if (j0 == 0) cons_trace(kEvCopyFirst, wave, lane);
     }
+    cons_trace(kEvCopyLast, wave, lane);
     fetched = read = kSteps;
-    done(lane);
+    active = false;
+    release(wave, lane);
   }
 
   // Overlapped schedule.
@@ -370,44 +494,57 @@ struct TileConsumer {
     v = *(const MIGEMM_LDS u32x4*)lds_at(slot_at + 16 * lane);
     pending = true;
   }
-  // Store the pending step's copy; after the tile's last step, release.
-  __device__ __forceinline__ void store_pending(int lane) {
+  // Store the pending step's copy.  After the tile's last step the tile is
+  // finished; its slot is released by the drain that follows the next
+  // tile's commit.
+  __device__ __forceinline__ void store_pending(int wave, int lane) {
     if (!uni(pending)) return;
     pending = false;
     const int j = uni(pend_j);
     store_copy(v, j, lane);
-    if (j == kSteps - 1) done(lane);
+    if (j == 0) cons_trace(kEvCopyFirst, wave, lane);
+    if (j == kSteps - 1) {
+      cons_trace(kEvCopyLast, wave, lane);
+      active = false;
+      finished = true;
+    }
   }
 
   // K-loop hook, right after the barrier.
   __device__ __forceinline__ void after_barrier(const KernelArgs& a, int wave, int lane) {
     (void)a;
-    store_pending(lane);
+    store_pending(wave, lane);
     if (!uni(active)) return;
     if (uni(fetched) > uni(read)) read_back_at(landing(wave, uni(read)), lane);
     if (uni(fetched) < kSteps) fetch(wave);
   }
-  // After a K loop: the copy steps the loop did not finish.  The ring and
-  // this wave's staging area are idle until this wave's epilogue (every
-  // wave passed the loop's closing barrier; the staging area is the wave's
-  // own), so all remaining fetches go out at once, into the staging area,
-  // and the drain waits for memory once.  A step fetched by the loop but not
-  // yet read back is still in its landing slot.
-  __device__ __forceinline__ void drain(const KernelArgs& a, int wave, int lane) {
-    (void)a;
+  // After the next tile's commit: the copy steps the K loop did not finish,
+  // then the release.  A step fetched by the loop but not yet read back is
+  // still in its landing slot (landed: the loop ended with vmcnt(0) and a
+  // barrier).  The rest go kConsumerDepth at a time through the landing
+  // slots: the staging area now holds the next tile, whose row statistics
+  // every wave still reads from it.
+  __device__ __forceinline__ void drain(int wave, int lane) {
     asm volatile("" : "+v"(lane));  // (as in begin: lane offsets computed here, not spilled)
-    store_pending(lane);
-    if (!uni(active)) return;
-    const int f0 = uni(fetched);
-    for (int j = f0; j < kSteps; ++j)
-      dma16_w5_nt(src, lds_at(drain_slot(wave, j)), at(lane_off, step_bytes, j));
-    fetched = kSteps;
-    wait_vmcnt<0>();
-    while (uni(active)) {
-      const int j = uni(read);
-      read_back_at(j < f0 ? landing(wave, j) : drain_slot(wave, j), lane);
-      store_pending(lane);
+    store_pending(wave, lane);
+    if (uni(active)) {
+      while (uni(read) < uni(fetched)) {
+        read_back_at(landing(wave, uni(read)), lane);
+        store_pending(wave, lane);
+      }
+      while (uni(active)) {
+        wait_lgkmcnt<0>();  // the landing slots' earlier read-backs have returned
+        const int f0 = uni(fetched);
+        const int n = kSteps - f0 < kConsumerDepth ? kSteps - f0 : kConsumerDepth;
+        for (int i = 0; i < n; ++i) fetch(wave);
+        wait_vmcnt<0>();
+        for (int i = 0; i < n; ++i) {
+          read_back_at(landing(wave, uni(read)), lane);
+          store_pending(wave, lane);
+        }
+      }
     }
+    if (uni(finished)) release(wave, lane);
   }
 };
 

@@ -44,10 +44,16 @@ constexpr int kConsumerEnd = kConsumerSlotOffset + kWaves * kConsumerDepth * kCo
 // next tile's K loop, fetching the tile back from D.
 enum ConsumerMode { kConsNone = 0, kConsStaged = 1, kConsOverlap = 2 };
 // Tile hand-off ring: two slots of {tile id, full count, empty count}.
+// After the slots: the hand-off debug block (debug header and trace
+// pointers, wait budget, forced wait, trace records per wave) and each
+// wave's trace record pointer for the tile its consumer works on, kept in
+// LDS rather than in registers across the K loop.
 constexpr int kHandoffSlots = 2;
 constexpr int kHandoffOffset = kConsumerEnd;
-constexpr int kHandoffBytes = 64;
-constexpr int kConsumerLdsBytes = kHandoffOffset + kHandoffBytes;     // 155712
+constexpr int kHandoffDebugOffset = kHandoffOffset + 32;
+constexpr int kHandoffRecOffset = kHandoffOffset + 64;
+constexpr int kHandoffBytes = 128;
+constexpr int kConsumerLdsBytes = kHandoffOffset + kHandoffBytes;     // 155776
 static_assert(kConsumerLdsBytes <= kLdsLimit, "consumer kernel LDS exceeds 160 KiB");
 
 struct KernelArgs {
@@ -78,7 +84,21 @@ struct KernelArgs {
   int32_t tiles_per_batch;
   int32_t pad2;
   int64_t a_bs_bytes, b_bs_bytes, c_bs_bytes, d_bs_bytes;
+  // Hand-off debugging (tile-consumer kernels; all zero when off): a header
+  // in the workspace ([0] ring waits that gave up, [1] the largest ring
+  // occupancy seen, in tiles), then kTraceWords 64-bit words per wave
+  // and tile of each workgroup (handoff.hpp), and the budget of a ring wait.
+  uint32_t* dbg;
+  uint64_t* trace;
+  int64_t spin_budget;     // s_memrealtime ticks (100 MHz) a ring wait may spin
+  int32_t trace_tiles;     // trace records per wave: ceil(tiles / grid)
+  int32_t force_wait;      // added to every acquire's target: a wait that cannot pass
 };
+
+// Hand-off debugging: the workspace's header, and the trace record of one
+// wave and tile (64-bit words; which word holds what: handoff.hpp).
+constexpr int kDebugHeaderBytes = 256;
+constexpr int kTraceWords = 16;
 
 // Stream-K workspace: per workgroup, one partial tile for the segment its
 // unit range starts in and one for the segment it ends in.

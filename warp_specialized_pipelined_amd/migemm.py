@@ -30,6 +30,7 @@ MIGEMM_NO_ALLOC_SCRATCH_BYTES = 64 << 20
 MIGEMM_F_TILE_CONSUMER = 0x1
 MIGEMM_F_STREAM_K = 0x2
 MIGEMM_F_STREAM_K_FORCE = 0x4
+MIGEMM_F_HANDOFF_DEBUG = 0x10
 MIGEMM_F_CONSUMER_OVERLAP = 0x8
 MIGEMM_TILE_M = 256
 MIGEMM_TILE_N = 256
@@ -37,7 +38,7 @@ MIGEMM_TILE_N = 256
 EXPORTED = [
     "gemm_desc_validate", "gemm_plan_create", "gemm_plan_destroy", "gemm_plan_get_info",
     "gemm_plan_workspace_size", "gemm_workspace_init", "gemm_run", "gemm_run_with_tile_consumer",
-    "gemm_run_no_alloc", "gemm_status_string",
+    "gemm_run_no_alloc", "gemm_debug_read", "gemm_status_string",
 ]
 
 
@@ -55,6 +56,17 @@ class migemm_desc(ctypes.Structure):
         ("L", ctypes.c_int64),
         ("a_bs", ctypes.c_int64), ("b_bs", ctypes.c_int64),
         ("c_bs", ctypes.c_int64), ("d_bs", ctypes.c_int64),
+        ("debug_wait_ticks", ctypes.c_int64), ("debug_force_wait", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+    ]
+
+
+class migemm_debug_info(ctypes.Structure):
+    _fields_ = [
+        ("waits_given_up", ctypes.c_uint32), ("max_occupancy", ctypes.c_uint32),
+        ("trace_offset", ctypes.c_int64),
+        ("grid", ctypes.c_int32), ("waves", ctypes.c_int32),
+        ("trace_tiles", ctypes.c_int32), ("trace_words", ctypes.c_int32),
     ]
 
 
@@ -110,6 +122,8 @@ def load(path: str = LIB_PATH):
     lib.gemm_run_with_tile_consumer.restype = i32
     lib.gemm_run_no_alloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp]
     lib.gemm_run_no_alloc.restype = i32
+    lib.gemm_debug_read.argtypes = [vp, vp, vp, P(migemm_debug_info)]
+    lib.gemm_debug_read.restype = i32
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -135,9 +149,10 @@ def _stream(s) -> int | None:
 
 def make_desc(M, N, K, a_type, b_type, a_rs, a_cs, b_rs, b_cs, c_rs, c_cs, d_rs, d_cs,
               device=0, flags=0, max_workgroups=0, c_type=MIGEMM_BF16, d_type=MIGEMM_BF16,
-              L=1, a_bs=0, b_bs=0, c_bs=0, d_bs=0):
+              L=1, a_bs=0, b_bs=0, c_bs=0, d_bs=0, debug_wait_ticks=0, debug_force_wait=0):
     return migemm_desc(M, N, K, a_type, b_type, c_type, d_type, a_rs, a_cs, b_rs, b_cs, c_rs, c_cs,
-                       d_rs, d_cs, device, flags, max_workgroups, 0, L, a_bs, b_bs, c_bs, d_bs)
+                       d_rs, d_cs, device, flags, max_workgroups, 0, L, a_bs, b_bs, c_bs, d_bs,
+                       debug_wait_ticks, debug_force_wait, 0)
 
 
 def gemm_status_string(status: int) -> str:
@@ -196,6 +211,14 @@ def gemm_run_no_alloc(plan, A, B, C, D, alpha: float, beta: float, stream=None,
     if check and st != MIGEMM_OK:
         raise MigemmError(st, "gemm_run_no_alloc")
     return int(st)
+
+
+def gemm_debug_read(plan, workspace, stream=None) -> tuple:
+    """(status, migemm_debug_info): synchronizes the stream, reads the debug
+    header.  status is MIGEMM_ERR_TIMEOUT when a bounded wait gave up."""
+    info = migemm_debug_info()
+    st = load().gemm_debug_read(plan, _ptr(workspace), _stream(stream), ctypes.byref(info))
+    return int(st), info
 
 
 def gemm_run_with_tile_consumer(plan, A, B, C, D, alpha: float, beta: float, row_sum, row_max,
