@@ -167,23 +167,34 @@ typedef struct migemm_plan_info {
 
 typedef struct migemm_plan migemm_plan; /* opaque, host memory only */
 
-/* Pure host check of a description (the pages' can_implement); needs no
- * device.  Returns MIGEMM_OK or the error code gemm_plan_create would give
- * before its device query. */
+/* Pure host check of a description; needs no device.  Returns MIGEMM_OK or
+ * the error code gemm_plan_create would give before its device query.
+ * Defined by: the kernel page (sm90_gemm_tma_warpspecialized_cooperative.hpp),
+ * can_implement -- may this kernel run these arguments (problem rank,
+ * tile-size and alignment rules), answered before any launch. */
 int gemm_desc_validate(const migemm_desc* desc);
 
 /* Validate, query the device (must be gfx950), choose the tile configuration
  * and the persistent grid, and return a plan in *out (set to NULL on error).
- * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED (strides), DEVICE. */
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED (strides), DEVICE.
+ * Defined by: the kernel page (sm90_gemm_tma_warpspecialized_cooperative.hpp),
+ * to_underlying_arguments (arguments -> kernel parameters, the persistent
+ * grid's size from the device's SM count in hw_info) and get_grid_shape;
+ * its device-side guard against the wrong architecture. */
 int gemm_plan_create(const migemm_desc* desc, migemm_plan** out);
 
-/* Free a plan (NULL is accepted). */
+/* Free a plan (NULL is accepted).  Host memory only; the pages have no
+ * counterpart (their Params live in the caller's object). */
 int gemm_plan_destroy(migemm_plan* plan);
 
-/* Copy the plan's choices into *out. */
+/* Copy the plan's choices into *out (grid, block, tiles, ring depths).
+ * Defined by: the kernel page (sm90_gemm_tma_warpspecialized_cooperative.hpp),
+ * get_grid_shape and get_block_shape, the launch geometry a caller queries. */
 int gemm_plan_get_info(const migemm_plan* plan, migemm_plan_info* out);
 
-/* Bytes of device workspace gemm_run needs (the pages' get_workspace_size).
+/* Bytes of device workspace gemm_run needs.  Defined by: the kernel page
+ * (sm90_gemm_tma_warpspecialized_cooperative.hpp), get_workspace_size -- the
+ * epilogue's and the tile scheduler's workspace (stream-K partials) summed.
  * Plans without stream-K tiles need none: 0, and `workspace` arguments below
  * may then be NULL.  A stream-K plan needs grid x 512 KiB of fp32 partial
  * tiles (two per workgroup) plus one 32-bit arrival counter per stream-K tile
@@ -191,8 +202,10 @@ int gemm_plan_get_info(const migemm_plan* plan, migemm_plan_info* out);
 size_t gemm_plan_workspace_size(const migemm_plan* plan);
 
 /* Make `workspace` (gemm_plan_workspace_size(plan) bytes of device memory,
- * 256-byte aligned, owned by the caller) ready for the plan's runs (the
- * pages' initialize_workspace): zeroes the arrival counters, with a kernel
+ * 256-byte aligned, owned by the caller) ready for the plan's runs.  Defined
+ * by: the kernel page (sm90_gemm_tma_warpspecialized_cooperative.hpp),
+ * initialize_workspace on a stream.  Zeroes the arrival counters (and a
+ * MIGEMM_F_HANDOFF_DEBUG plan's whole debug area), with a kernel
  * enqueued on `stream` (so it may be captured in a HIP graph).  Every run
  * that completes leaves the counters at zero again; call this before the
  * first run, after a run that did not complete, and before a workspace is
@@ -202,7 +215,12 @@ size_t gemm_plan_workspace_size(const migemm_plan* plan);
 int gemm_workspace_init(const migemm_plan* plan, void* workspace, void* stream);
 
 /* D = alpha*A*B + beta*C, enqueued on `stream` (a hipStream_t; NULL = the
- * null stream).  A, B, D must be non-NULL and 16-byte aligned; C may be NULL
+ * null stream).  Defined by: the kernel page
+ * (sm90_gemm_tma_warpspecialized_cooperative.hpp), the persistent kernel's
+ * body -- each CTA takes output tiles from the tile scheduler, its producer
+ * loads K stages into a multi-stage ring that its consumers drain into
+ * accumulators, and the epilogue forms alpha * accumulator + beta * C (C
+ * loaded only when needed) and stores D.  A, B, D must be non-NULL and 16-byte aligned; C may be NULL
  * only when beta == 0, in which case C is never read (it may hold NaN).
  * With K == 0, D = beta*C.  M == 0 or N == 0 is a no-op.  C may alias D only
  * with identical strides.  Asynchronous: returns once the kernel is queued.
@@ -216,7 +234,13 @@ int gemm_run(const migemm_plan* plan, const void* A, const void* B, const void* 
              float alpha, float beta, void* workspace, void* stream);
 
 /* gemm_run, and in the same kernel a consumer stage fed through a 2-slot
- * tile hand-off ring: every finished 256 x 256 tile of D is committed by the
+ * tile hand-off ring.  Defined by: CUTLASS issue #2900 ("How to build a
+ * pipeline between epilogue and communication warp groups?"), the requested
+ * protocol -- producer acquire, store the tile, commit; consumer wait, work
+ * on the tile, release -- with the producer's first acquires passing at once
+ * (the kernel page starts producer pipeline states at the opposite phase;
+ * the CuTe DSL task_scheduling.pipeline page names producer_acquire,
+ * producer_commit and consumer_release): every finished 256 x 256 tile of D is committed by the
  * waves that stored it; the consumer work waits for the commit, reads the
  * tile as the epilogue staged it in LDS (with MIGEMM_F_CONSUMER_OVERLAP the
  * copy instead reads it back from D while the next tile's main loop runs),
@@ -263,7 +287,10 @@ typedef struct migemm_debug_info {
 } migemm_debug_info;
 
 /* Synchronizes `stream`, then reads the debug header of a
- * MIGEMM_F_HANDOFF_DEBUG plan's workspace into *out.  Returns
+ * MIGEMM_F_HANDOFF_DEBUG plan's workspace into *out.  The waits it reports
+ * on are those of the hand-off protocol of CUTLASS issue #2900 (producer
+ * acquire, consumer wait), bounded here so that a protocol fault ends as a
+ * status rather than a hang.  Returns
  * MIGEMM_ERR_TIMEOUT if a bounded ring wait has given up since the last
  * gemm_workspace_init, else MIGEMM_OK (or INVALID_ARG for a plan without
  * the flag, a NULL argument; DEVICE if the copy fails). */
@@ -290,7 +317,7 @@ int gemm_debug_read(const migemm_plan* plan, const void* workspace, void* stream
 int gemm_run_no_alloc(const migemm_plan* plan, const void* A, const void* B, const void* C,
                       void* D, float alpha, float beta, void* stream);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL).  No counterpart on the pages. */
 const char* gemm_status_string(int status);
 
 #ifdef __cplusplus
