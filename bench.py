@@ -531,6 +531,34 @@ def main():
                              wc.flops, 8192)
             del pc, Dc
         configs[w.name] = extra["interleaved_8192"]["staged"]
+        # The source C of the beta = 0.5 workload: read during the K loop's
+        # last two iterations (the plan's choice here) or in the epilogue,
+        # against the same GEMM with beta = 0, interleaved x 5.
+        w2 = synth.WORKLOADS[1]
+        p2 = Problem.from_workload(w2).to_device()
+        D2 = p2.new_d(0.0)
+        plan_k = migemm.Plan(p2.desc())
+        plan_e = migemm.Plan(p2.desc(flags=migemm.MIGEMM_F_C_IN_EPILOGUE))
+        fc = {"c_in_k_loop": lambda: migemm.gemm_run(plan_k.handle, p2.dA, p2.dB, p2.dC, D2, 1.0,
+                                                       p2.beta, None, stream),
+              "c_in_epilogue": lambda: migemm.gemm_run(plan_e.handle, p2.dA, p2.dB, p2.dC, D2, 1.0,
+                                                         p2.beta, None, stream),
+              "beta_zero": lambda: migemm.gemm_run(plan_k.handle, p2.dA, p2.dB, None, D2, 1.0, 0.0,
+                                                   None, stream)}
+        settle(fc["c_in_k_loop"], stream, 0.3)
+        tc = {k: [] for k in fc}
+        for _ in range(5):
+            for name, fn in fc.items():
+                fn()
+                tc[name] += per_launch_ms(fn, max(10, args.steps // 2), stream)
+        mc = {k: statistics.median(v) for k, v in tc.items()}
+        extra["c_read_" + w2.name] = {
+            "plan_reads_c_in_k_loop": int(plan_k.info.c_in_k_loop),
+            **{k + "_median_us": round(1e3 * v, 2) for k, v in mc.items()},
+            "c_in_k_loop_over_beta_zero": round(mc["c_in_k_loop"] / mc["beta_zero"], 4),
+            "c_in_epilogue_over_beta_zero": round(mc["c_in_epilogue"] / mc["beta_zero"], 4),
+        }
+        del p2, D2
         extra["workloads"] = configs
         w8 = synth.WORKLOADS[4]
         extra["fp8_gemm_tflops"] = configs[w8.name]["tflops_at_median"]

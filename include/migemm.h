@@ -96,6 +96,16 @@ typedef enum migemm_status {
  * debug_force_wait > 0 adds that much to every acquire's target: a wait
  * that cannot pass, for testing the bounded wait itself. */
 #define MIGEMM_F_HANDOFF_DEBUG 0x10u
+/* Where gemm_run reads C (beta != 0).  With this flag: in the epilogue, after
+ * the tile's K loop.  Without it, a plan whose workgroups each take one round
+ * of whole tiles (tiles <= grid, not stream-K, K at least two stages) reads C
+ * into LDS during the K loop's last two iterations, as the ring's slots fall
+ * free -- the kernel page's separate C-load role, here taken by the MMA
+ * waves -- so that half the read overlaps the last stages' MFMAs instead of
+ * waiting in the epilogue; other plans read it in the epilogue.  The tile
+ * consumer always reads C in the epilogue.  gemm_plan_get_info reports the
+ * choice (c_in_k_loop).  Same results bit for bit either way. */
+#define MIGEMM_F_C_IN_EPILOGUE 0x20u
 
 /* Output tile of the persistent scheduler (and the hand-off unit). */
 #define MIGEMM_TILE_M 256
@@ -161,7 +171,8 @@ typedef struct migemm_plan_info {
   int32_t handoff_slots;   /* depth of the tile hand-off ring */
   int64_t stream_k_tiles;  /* tiles cut into K ranges (0: every tile is taken whole) */
   int32_t stream_k_units_per_tile; /* K stages (tile_k each) per such tile */
-  int32_t reserved;
+  int32_t c_in_k_loop;     /* 1: with beta != 0, gemm_run reads C in the K loop's last two
+                              iterations (else in the epilogue); see MIGEMM_F_C_IN_EPILOGUE */
   int64_t batches;         /* L (1 for one product) */
 } migemm_plan_info;
 

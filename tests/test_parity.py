@@ -147,6 +147,30 @@ def test_alpha_beta(alpha, beta):
     assert ok(check_full(p, D))
 
 
+@pytest.mark.parametrize("M,N,K,la,lb", [
+    (300, 280, 264, "row", "col"),     # ragged tiles, K stages 5 (last ragged)
+    (1000, 1200, 520, "row", "row"),   # several tiles per workgroup
+    (512, 512, 64, "col", "row"),      # one K stage: C is read in the epilogue
+    (512, 384, 72, "row", "col"),      # two K stages, the second ragged
+    (640, 520, 2048, "col", "col"),
+])
+def test_c_read_schedules_agree(M, N, K, la, lb):
+    """beta != 0: C loaded in the K loop's last two iterations (default) or
+    in the epilogue (MIGEMM_F_C_IN_EPILOGUE) -- the same D bit for bit, and
+    within the bound."""
+    g = torch.Generator().manual_seed(M + K)
+    p = Problem.random(g, M, N, K, la, lb, dist="normal", alpha=0.75, beta=-0.5).to_device()
+    plan = plan_for(p)
+    plan_e = plan_for(p, flags=migemm.MIGEMM_F_C_IN_EPILOGUE)
+    assert plan.info.c_in_k_loop == int(plan.info.num_tiles <= plan.info.grid and K > 64)
+    assert plan_e.info.c_in_k_loop == 0
+    D1 = p.run(plan)
+    D2 = p.run(plan_e)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+    assert ok(check_full(p, D1))
+
+
 def test_column_major_d_and_c():
     g = torch.Generator().manual_seed(5)
     p = Problem.random(g, 300, 200, 136, "row", "row", dist="normal", alpha=1.0, beta=0.75,

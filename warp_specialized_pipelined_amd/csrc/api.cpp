@@ -83,7 +83,7 @@ int validate(const migemm_desc* d, Canon* out) {
     return MIGEMM_ERR_INVALID_ARG;
   constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
   if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | MIGEMM_F_HANDOFF_DEBUG |
-                    kStreamK)) != 0)
+                    MIGEMM_F_C_IN_EPILOGUE | kStreamK)) != 0)
     return MIGEMM_ERR_INVALID_ARG;
   if ((d->flags & MIGEMM_F_HANDOFF_DEBUG) && !(d->flags & MIGEMM_F_TILE_CONSUMER))
     return MIGEMM_ERR_INVALID_ARG;
@@ -243,6 +243,7 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   a.c_bs_bytes = c.c_bs * 2;
   a.d_bs_bytes = c.d_bs * 2;
   a.group_m = a.tiles_m < 8 ? (a.tiles_m > 0 ? a.tiles_m : 1) : 8;
+  a.c_preload = 0;
   a.stat_ld = a.tiles_n;
 
   int grid = p->cu_count;
@@ -270,6 +271,14 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
     grid = a.num_tiles;
   }
   p->grid = grid;
+  // The source C in the K loop's last two iterations pays where every
+  // workgroup takes one round of whole tiles: C's read is then the kernel's
+  // tail on every compute unit at once, and half of it moves under the last
+  // stages' MFMAs (4096^3 with beta != 0: 6.2% over beta = 0 instead of
+  // 7.9%).  With more rounds the extra loads in iteration KT-2 cost more than
+  // they hide (8192^3: 4.8% instead of 2.8%).
+  a.c_preload = !(desc->flags & MIGEMM_F_C_IN_EPILOGUE) && !p->sel.stream_k &&
+                a.num_tiles <= grid && kt >= 2;
   if (desc->flags & MIGEMM_F_HANDOFF_DEBUG) {
     p->debug = true;
     p->trace_tiles = grid > 0 ? (a.num_tiles + grid - 1) / grid : 0;
@@ -327,6 +336,7 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
   out->handoff_slots = migemm::kHandoffSlots;
   out->stream_k_tiles = p->sel.stream_k ? p->base.num_tiles - p->base.sk_first : 0;
   out->stream_k_units_per_tile = p->sel.stream_k ? p->base.sk_kt : 0;
+  out->c_in_k_loop = p->base.c_preload;
   out->batches = p->base.tiles_per_batch > 0 ? p->base.num_tiles / p->base.tiles_per_batch
                                              : (p->desc.L > 1 ? p->desc.L : 1);
   return MIGEMM_OK;

@@ -44,15 +44,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
   if constexpr (CONS == kConsNone) {
     NoSideWork none;
     const int whole = SK ? a.sk_first : a.num_tiles;  // tiles taken whole
-    for (int L = first; L < whole; L += gridDim.x) {
-      const TileCoord t = tile_of(L, a);
-      const KernelArgs ab = batch_args(a, t.l);
-      const LaneIds id(lane, wave);
-      mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
-      const LaneIds ie(lane, wave);
-      epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
-      wait_lgkmcnt<0>();  // staging reads done ...
-      barrier();          // ... in every wave before the ring is refilled
+    if (!SK && a.C != nullptr && a.c_preload) {
+      // beta != 0: the last two K iterations load the tile's C into LDS
+      // (CPreload), when the K loop has at least two stages.
+      const bool preload = (a.K + StageGeom<ES>::kK - 1) / StageGeom<ES>::kK >= 2;
+      for (int L = first; L < whole; L += gridDim.x) {
+        const TileCoord t = tile_of(L, a);
+        const KernelArgs ab = batch_args(a, t.l);
+        const LaneIds id(lane, wave);
+        CPreload pre;
+        mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, pre);
+        const LaneIds ie(lane, wave);
+        epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane, preload);
+        wait_lgkmcnt<0>();
+        barrier();
+      }
+    } else {
+      for (int L = first; L < whole; L += gridDim.x) {
+        const TileCoord t = tile_of(L, a);
+        const KernelArgs ab = batch_args(a, t.l);
+        const LaneIds id(lane, wave);
+        mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
+        const LaneIds ie(lane, wave);
+        epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
+        wait_lgkmcnt<0>();  // staging reads done ...
+        barrier();          // ... in every wave before the ring is refilled
+      }
     }
     if constexpr (SK) {
       // When every tile is split (no whole-tile rounds before), the slot is

@@ -81,6 +81,14 @@ __device__ __forceinline__ void dma16_w5_nt(__amdgpu_buffer_rsrc_t r, lds_u8* ld
                : "memory");
 }
 
+// 5 wait states, default cache policy.
+__device__ __forceinline__ void dma16_w5(__amdgpu_buffer_rsrc_t r, lds_u8* lds, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(r),
+               "{m0}"(m0)
+               : "memory");
+}
+
 // Cache-policy operand of the buffer load/store builtins: the non-temporal
 // hint (nt) for data this kernel writes and does not read back soon; device
 // scope (sc1) for data other XCDs read during the kernel -- the encoding of

@@ -278,6 +278,8 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // workgroup's last tile has no K loop after it and is copied from its
 // staging area.
 struct TileConsumer {
+  static constexpr bool kLoadsC = false;        // the epilogue loads C itself
+  __device__ __forceinline__ void c_load(const KernelArgs&, int, int, uint32_t, int) {}
   static constexpr int kSteps = kWaveTile / 4;  // 64 rows per wave, 2 per step: 32
   // Buffer resources from the tile's origin: D (fetch) and D_copy (store)
   // share their layout, so one offset serves both; the statistics have one

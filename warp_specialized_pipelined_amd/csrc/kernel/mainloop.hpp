@@ -142,9 +142,13 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 // Work that rides along in the K loop: once per iteration, right after the
 // barrier (before the iteration's stage loads), after_barrier() issues its
-// memory operations.
+// memory operations.  A side work with kLoadsC also takes over the last two
+// iterations' loads (see mainloop_range): c_load(x) loads the epilogue's
+// source C into LDS byte x of the staging layout.
 struct NoSideWork {
+  static constexpr bool kLoadsC = false;
   __device__ __forceinline__ void after_barrier(const KernelArgs&, int, int) {}
+  __device__ __forceinline__ void c_load(const KernelArgs&, int, int, uint32_t, int) {}
 };
 
 // Stage geometry for element size ES.
@@ -522,10 +526,25 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     barrier();
     f.template read_part<0, 0, 1>(0, kB);
   }
+  // The epilogue's source C (side work with kLoadsC): the two ring slots
+  // fall free in the last two iterations, and the epilogue stages its tile
+  // over them.  So the loads of stages past K that those iterations would
+  // issue (they only zero a free slot) give way to loads of C, straight into
+  // the staging layout: iteration KT-2 fills the slot it frees (and the
+  // staging area's tail past the ring), iteration KT-1 the other one, and
+  // the loop's closing wait covers both.  bf16's first k-step of iteration
+  // KT-1 would load B of stage KT into the slot C already holds: skipped.
+  constexpr bool kLoadsC = SideWork::kLoadsC;
+  constexpr int kCLoads = 18;  // C loads per wave in iteration KT-2: 16 into the slot, 2 into the tail
   auto iteration = [&](const int d, auto mask_c) {
     constexpr bool kMask = decltype(mask_c)::value;
     const uint32_t cur = (d & 1) * kStageBytes;
     const uint32_t nxt = ((d + 1) & 1) * kStageBytes;
+    bool c_here = false, skip_b = false;
+    if constexpr (kMask && kLoadsC) {
+      c_here = KT >= 2 && d >= KT - 2;
+      skip_b = KT >= 2 && d == KT - 1;
+    }
     int krem_a, krem_b;
     const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(k0 + d + 2, K, &krem_a);
     const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(k0 + (kBf16 ? d + 1 : d + 2), K, &krem_b);
@@ -536,7 +555,9 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
       // MFMA (in two bursts of six reads it was 1% slower).
       if constexpr (m % 2 == 0 && m < 8) f.template read_part<1, m / 2, 4>(cur, cur + kB);
       f.template mma<0, m, 1>(acc);
-      if constexpr (kBf16 && (m & 1)) lb.template load<kMask>(rb, krem_b, nxt + kB, wave, m >> 1);
+      if constexpr (kBf16 && (m & 1)) {
+        if (!skip_b) lb.template load<kMask>(rb, krem_b, nxt + kB, wave, m >> 1);
+      }
     });
     static_for<1, kLast>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
@@ -552,8 +573,15 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     });
     sched_fence();
     // The last k-step's fragments are in registers: this wave is done
-    // reading stage d once its reads have returned.
-    wait_vmcnt<0>();
+    // reading stage d once its reads have returned.  (In iteration KT-1 of a
+    // C-loading side work the only loads in flight are the kCLoads of C from
+    // iteration KT-2, and stage KT is past K: they may stay in flight until
+    // the loop's closing wait.)
+    if (skip_b) {
+      wait_vmcnt<kCLoads>();
+    } else {
+      wait_vmcnt<0>();
+    }
     wait_lgkmcnt<0>();
     if constexpr (kMask) clear_tail(d + 1, nxt);
     barrier();
@@ -565,7 +593,14 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
       if constexpr (m % 2 == 0 && m >= 2 && m < 10)
         f.template read_part<0, (m - 2) / 2, 4>(nxt, nxt + kB);
       f.template mma<kLast & 1, m, 1>(acc);
-      if constexpr (kBf16) {
+      if (c_here) {
+        // 64 loads of 1 KiB fill the freed slot, 16 per wave, one behind
+        // each MFMA; in iteration KT-2 two more per wave fill the tail.
+        side.c_load(a, tm, tn, cur + 1024 * (16 * wave + m), lane);
+        if constexpr (m < 2) {
+          if (d == KT - 2) side.c_load(a, tm, tn, kRingBytes + 1024 * (2 * wave + m), lane);
+        }
+      } else if constexpr (kBf16) {
         if constexpr (m & 1) la.template load<kMask>(ra, krem_a, cur, wave, m >> 1);
       } else {
         if constexpr (m < 8) la.template load<kMask>(ra, krem_a, cur, wave, m);

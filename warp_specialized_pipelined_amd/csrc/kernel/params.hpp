@@ -82,7 +82,7 @@ struct KernelArgs {
   // Batches: tiles are numbered batch after batch (tiles_per_batch each);
   // matrix l of an operand starts l * stride bytes after its pointer.
   int32_t tiles_per_batch;
-  int32_t pad2;
+  int32_t c_preload;   // beta != 0: load C in the K loop's last two iterations (CPreload)
   int64_t a_bs_bytes, b_bs_bytes, c_bs_bytes, d_bs_bytes;
   // Hand-off debugging (tile-consumer kernels; all zero when off): a header
   // in the workspace ([0] ring waits that gave up, [1] the largest ring

@@ -31,6 +31,7 @@ MIGEMM_F_TILE_CONSUMER = 0x1
 MIGEMM_F_STREAM_K = 0x2
 MIGEMM_F_STREAM_K_FORCE = 0x4
 MIGEMM_F_HANDOFF_DEBUG = 0x10
+MIGEMM_F_C_IN_EPILOGUE = 0x20
 MIGEMM_F_CONSUMER_OVERLAP = 0x8
 MIGEMM_TILE_M = 256
 MIGEMM_TILE_N = 256
@@ -79,7 +80,7 @@ class migemm_plan_info(ctypes.Structure):
         ("swapped", ctypes.c_int32), ("a_kmajor", ctypes.c_int32), ("b_kmajor", ctypes.c_int32),
         ("cu_count", ctypes.c_int32), ("handoff_slots", ctypes.c_int32),
         ("stream_k_tiles", ctypes.c_int64), ("stream_k_units_per_tile", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("batches", ctypes.c_int64),
+        ("c_in_k_loop", ctypes.c_int32), ("batches", ctypes.c_int64),
     ]
 
 
