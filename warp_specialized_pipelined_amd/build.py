@@ -1,7 +1,7 @@
 """Build libmigemm.so in-tree with hipcc for gfx950.
 
-    python -m warp_specialized_pipelined_amd.build          # build
-    python -m warp_specialized_pipelined_amd.build --asm    # also dump AMD assembly
+    python -m warp_specialized_pipelined_amd.build                # build
+    python -m warp_specialized_pipelined_amd.build --asm DIR      # also write the AMD assembly to DIR
 
 The library is written next to this file so that it travels with the source
 tree; nothing is installed.
@@ -62,4 +62,7 @@ def dump_asm(out_dir: str) -> str:
 if __name__ == "__main__":
     print(build(verbose=True))
     if "--asm" in sys.argv:
-        print(dump_asm(os.path.join(os.path.dirname(HERE), "_work", "asm")))
+        i = sys.argv.index("--asm")
+        if i + 1 >= len(sys.argv):
+            sys.exit("--asm needs an output directory")
+        print(dump_asm(sys.argv[i + 1]))
