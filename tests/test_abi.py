@@ -40,6 +40,25 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_library_shares_torchs_hip_runtime():
+    """torch carries its own HIP runtime library; loading the binding first
+    must still leave exactly one HIP runtime in the process (torch's), or the
+    library could not use torch's device memory and streams."""
+    import sys
+    prog = ("import sys; sys.path.insert(0, %r)\n"
+            "from warp_specialized_pipelined_amd import migemm\n"
+            "migemm.load()\n"
+            "import torch, os\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = sorted({os.path.realpath(l.split()[-1]) for l in maps if 'libamdhip64' in l})\n"
+            "print(repr((libs, os.path.realpath(os.path.dirname(torch.__file__)))))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", prog], capture_output=True, text=True, check=True,
+                         timeout=300).stdout
+    libs, torch_dir = eval(out.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
+    assert libs[0].startswith(torch_dir + os.sep), (libs, torch_dir)
+
+
 def test_struct_layout_matches_c():
     prog = r"""
 #include <stdio.h>

@@ -93,11 +93,22 @@ class MigemmError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load libmigemm.so (once).  Raises if it is missing."""
+def load(path: str | None = None):
+    """Load libmigemm.so (once; LIB_PATH unless a path is given).  Raises if
+    it is missing.
+
+    torch ships its own HIP runtime library.  It is imported first, when it
+    is installed, so that libmigemm.so binds that same runtime: with two HIP
+    runtimes in one process the second cannot use the device, and torch's
+    device pointers and streams would not be valid in it."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m warp_specialized_pipelined_amd.build`"
                            " (or __graft_entry__.build())")
