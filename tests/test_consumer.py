@@ -2,8 +2,9 @@
 
 gemm_run_with_tile_consumer must give the same D as gemm_run, bit for bit;
 its consumer outputs have exactly one correct value given that D: a bit copy
-of D, and per 256-column tile slice of every row an fp32 sum in the fixed
-chunk-then-tree order and the largest non-NaN value (-0 < +0), which the
+of D, and per 256-column tile slice of every row the fp32 sum taken one
+column at a time in ascending order from +0.0 and the largest non-NaN value
+(-0 < +0), which the
 oracle recomputes from the GPU's own D and which must match exactly.
 Outputs are poisoned first with a NaN whose payload no result can carry
 (results derived from bf16 values have zero low 16 bits), so an unconsumed
