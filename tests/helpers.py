@@ -1,11 +1,14 @@
 """Shared test plumbing: run the HIP GEMM through the C ABI on seeded inputs
-and judge the result with the CPU oracle."""
+and judge the result with the CPU oracle.
+
+The oracle is imported where a result is judged, not at module import:
+bench.py draws its inputs with Problem too, and its timed path must not load
+the oracle (only its CPU-baseline leg does)."""
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-import oracle
 from warp_specialized_pipelined_amd import migemm, synth
 
 BF16, E4M3 = synth.BF16, synth.E4M3
@@ -21,7 +24,13 @@ def codes(t: torch.Tensor) -> np.ndarray:
     raise TypeError(t.dtype)
 
 
-def oracle_operand(t: torch.Tensor, rs: int, cs: int) -> oracle.Operand:
+def _oracle():
+    import oracle
+    return oracle
+
+
+def oracle_operand(t: torch.Tensor, rs: int, cs: int):
+    oracle = _oracle()
     dt = oracle.BF16 if t.dtype == torch.bfloat16 else oracle.E4M3
     return oracle.Operand(dt, codes(t), rs, cs)
 
@@ -117,21 +126,23 @@ class Problem:
 
     def oracle_full(self, nthreads=0):
         Aop, Bop, Cop = self.oracle_ops()
-        return oracle.gemm(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta, nthreads)
+        return _oracle().gemm(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta,
+                              nthreads)
 
     def oracle_entries(self, rows, cols, nthreads=0):
         Aop, Bop, Cop = self.oracle_ops()
-        return oracle.gemm_entries(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta,
-                                   rows, cols, nthreads)
+        return _oracle().gemm_entries(self.M, self.N, self.K, Aop, Bop, Cop, self.alpha, self.beta,
+                                      rows, cols, nthreads)
 
     def d_values(self, D: torch.Tensor) -> np.ndarray:
         """GPU D (bf16) widened exactly to float64, as a logical M x N array."""
-        v = oracle.bf16_codes_to_f64(codes(D)).reshape(self.d_shape)
+        v = _oracle().bf16_codes_to_f64(codes(D)).reshape(self.d_shape)
         if self.d_layout == "row":
             return v[:, :self.N]
         return v[:, :self.M].T
 
     def in_dtype(self):
+        oracle = _oracle()
         return oracle.BF16 if self.dtype == BF16 else oracle.E4M3
 
 
@@ -139,7 +150,7 @@ def check_full(p: Problem, D: torch.Tensor, ref_absum=None):
     """Every output element against the oracle (ref_absum: a result of
     p.oracle_full() computed before, to reuse)."""
     ref, absum = ref_absum if ref_absum is not None else p.oracle_full()
-    return oracle.check(p.d_values(D), ref, absum, p.in_dtype(), p.alpha)
+    return _oracle().check(p.d_values(D), ref, absum, p.in_dtype(), p.alpha)
 
 
 _WORKLOAD_REF = {}

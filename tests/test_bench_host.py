@@ -43,3 +43,36 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""   # no JSON line: nothing was measured
+
+
+def test_only_the_cpu_baseline_leg_imports_the_oracle():
+    """The oracle is test infrastructure: bench.py may load it for its CPU
+    baseline only.  Statically, every import of it sits in cpu_baseline();
+    at run time, importing bench and drawing and describing the workload
+    (what the timed path does before it launches) leaves it unloaded."""
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    owners = {}
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            for node in ast.walk(fn):
+                if isinstance(node, (ast.Import, ast.ImportFrom)):
+                    owners.setdefault(id(node), fn.name)
+    for node in ast.walk(tree):
+        names = []
+        if isinstance(node, ast.Import):
+            names = [a.name for a in node.names]
+        elif isinstance(node, ast.ImportFrom):
+            names = [node.module or ""] + [a.name for a in node.names]
+        if any(n == "oracle" or n.startswith("oracle.") or n == "oracle_operand" for n in names):
+            assert owners.get(id(node)) == "cpu_baseline", (node.lineno, names)
+    prog = ("import sys; sys.path.insert(0, %r); sys.argv = ['bench.py']\n"
+            "import bench\n"
+            "from tests.helpers import Problem\n"
+            "from warp_specialized_pipelined_amd import synth\n"
+            "for w in synth.WORKLOADS[:3]:\n"
+            "    Problem.from_workload(w).desc()\n"
+            "print('oracle' in sys.modules)\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", prog], capture_output=True, text=True, check=True,
+                         timeout=300).stdout
+    assert out.strip().splitlines()[-1] == "False"
