@@ -264,7 +264,7 @@ def observe_clock(step, stream, ms_per_step, seconds=1.5, period=0.01):
     """Run `step` back to back for about `seconds` while a thread samples the
     shader clock (and the board power, where hwmon reports it) every
     `period` s.  Returns the median clock, the throughput of that run and
-    the sample counts; None where the driver exposes nothing."""
+    the sample counts; None where amdgpu's sysfs exposes no clock."""
     import glob
     import statistics
     import threading
@@ -385,7 +385,7 @@ def config_figures(w, ms_list, consumer=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import statistics

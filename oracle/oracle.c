@@ -17,7 +17,7 @@
  * alpha*acc + beta*C; CUTLASS SM90 cooperative kernel header, "Type Aliases"
  * and the consumer warp-group epilogue call).  They do not fix numerics; the
  * accumulation is done here in fp64 so that the result is exact or within a
- * few fp64 ulps of the exact rational value, and the GPU is judged against it
+ * few fp64 ulps of the exact rational value, and the GPU result is checked against it
  * with the tolerance stated next to each config.
  *
  * The beta term is skipped, and C never read, when beta == 0 (the epilogue of

@@ -7,4 +7,4 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")

@@ -1,7 +1,7 @@
 """Shared test plumbing: run the HIP GEMM through the C ABI on seeded inputs
-and judge the result with the CPU oracle.
+and check the result with the CPU oracle.
 
-The oracle is imported where a result is judged, not at module import:
+The oracle is imported where a result is checked, not at module import:
 bench.py draws its inputs with Problem too, and its timed path must not load
 the oracle (only its CPU-baseline leg does)."""
 from __future__ import annotations
