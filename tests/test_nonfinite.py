@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from warp_specialized_pipelined_amd import migemm, synth
-from tests.helpers import Problem
+from tests.helpers import Problem, codes
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,38 @@ def test_bf16_nan_and_infinities_propagate(la, lb):
     n_nan, n_inf, n_fin = check_classes(p, D)
     print(f"[nonfinite] bf16 {la}/{lb}: {n_nan} NaN, {n_inf} inf, {n_fin} finite outputs", flush=True)
     assert n_nan > 2 * N and n_inf > N
+
+    # Stream-K: the specials meet in partial sums and in the fixup's adds.
+    pk = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_STREAM_K_FORCE))
+    ws = torch.empty(pk.workspace_size, dtype=torch.uint8, device="cuda")
+    migemm.gemm_workspace_init(pk.handle, ws)
+    Dk = p.new_d()
+    migemm.gemm_run(pk.handle, p.dA, p.dB, p.dC, Dk, p.alpha, p.beta, ws)
+    torch.cuda.synchronize()
+    check_classes(p, Dk)
+
+    # The tile consumer (row-major D only): D bit for bit as gemm_run's, the
+    # copy bit for bit, and the row statistics over NaN and infinite values
+    # exactly as the oracle recomputes them from D.
+    if p.d_layout == "row":
+        pc = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_CONSUMER))
+        tn = -(-N // 256)
+        D2 = p.new_d()
+        Dc = torch.full_like(D2, float("nan"))
+        rs = torch.full((M, tn), 1.0, dtype=torch.float32, device="cuda")
+        rm = torch.full_like(rs, 1.0)
+        migemm.gemm_run_with_tile_consumer(pc.handle, p.dA, p.dB, p.dC, D2, p.alpha, p.beta, rs,
+                                           rm, Dc)
+        torch.cuda.synchronize()
+        assert torch.equal(D2.view(torch.int16), D.view(torch.int16))
+        assert torch.equal(Dc.view(torch.int16)[:, :N], D.view(torch.int16)[:, :N])
+        dc = codes(D).reshape(p.d_shape)
+        want_s, want_m = oracle.tile_rowstats(dc, M, N, p.d_rs, p.d_cs, 256)
+        got_s, got_m = rs.cpu().numpy(), rm.cpu().numpy()
+        assert np.array_equal(classify(got_s), classify(want_s))
+        fs = np.isfinite(want_s)
+        assert np.array_equal(got_s[fs].view(np.uint32), want_s[fs].view(np.uint32))
+        assert np.array_equal(np.where(got_m == 0, 0, got_m), np.where(want_m == 0, 0, want_m))
 
 
 @pytest.mark.parametrize("la,lb", [("row", "row"), ("row", "col")])
