@@ -26,7 +26,9 @@
  *   - every device pointer is owned by the caller; the library never
  *     allocates device memory, never frees, and never synchronizes a stream;
  *   - a plan owns host memory only and is immutable after creation; one plan
- *     may be run concurrently on several streams;
+ *     may be run concurrently on several streams; every entry point taking a
+ *     plan first checks that it is live (created and not yet destroyed) and
+ *     gives MIGEMM_ERR_INVALID_ARG otherwise, without reading it;
  *   - every call returns a migemm_status (0 = OK, negative = error) and never
  *     throws.  Argument, device and alignment errors are found before
  *     anything is launched; a launch failure reported by the HIP runtime gives
@@ -194,8 +196,10 @@ int gemm_desc_validate(const migemm_desc* desc);
  * its device-side guard against the wrong architecture. */
 int gemm_plan_create(const migemm_desc* desc, migemm_plan** out);
 
-/* Free a plan (NULL is accepted).  Host memory only; the pages have no
- * counterpart (their Params live in the caller's object). */
+/* Free a plan (NULL is accepted and does nothing).  A pointer that is not a
+ * live plan (destroyed already, or never created) gives INVALID_ARG and
+ * frees nothing.  Host memory only; the pages have no counterpart (their
+ * Params live in the caller's object). */
 int gemm_plan_destroy(migemm_plan* plan);
 
 /* Copy the plan's choices into *out (grid, block, tiles, ring depths).

@@ -232,6 +232,27 @@ def test_null_arguments_are_rejected_without_a_device():
     assert lib.gemm_workspace_init(None, None, None) == migemm.MIGEMM_ERR_INVALID_ARG
 
 
+def test_pointers_that_are_not_live_plans_are_rejected_unread():
+    # A host buffer that was never a plan, filled with bytes that would make
+    # wild kernel arguments: every entry point must refuse it before reading
+    # it (the library checks a plan against the plans alive in the process).
+    import ctypes
+    lib = migemm.load()
+    junk = ctypes.create_string_buffer(b"\xff" * 4096)
+    fake = ctypes.addressof(junk)
+    bad = migemm.MIGEMM_ERR_INVALID_ARG
+    assert lib.gemm_run(fake, None, None, None, None, 1.0, 0.0, None, None) == bad
+    assert lib.gemm_run_with_tile_consumer(fake, None, None, None, None, 1.0, 0.0, None, None,
+                                           None, None, None) == bad
+    assert lib.gemm_run_no_alloc(fake, None, None, None, None, 1.0, 0.0, None) == bad
+    assert lib.gemm_plan_get_info(fake, ctypes.byref(migemm.migemm_plan_info())) == bad
+    assert lib.gemm_workspace_init(fake, fake, None) == bad
+    assert lib.gemm_debug_read(fake, fake, None, ctypes.byref(migemm.migemm_debug_info())) == bad
+    assert migemm.gemm_plan_workspace_size(fake) == 0
+    assert lib.gemm_plan_destroy(fake) == bad          # nothing freed
+    assert junk.raw == b"\xff" * 4096 + b"\x00"
+
+
 @pytest.mark.skipif(have_gpu(), reason="checks the no-device path")
 def test_plan_create_without_a_gpu_reports_device_error():
     with pytest.raises(migemm.MigemmError) as e:

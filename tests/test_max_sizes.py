@@ -123,7 +123,8 @@ def test_k_contiguous_a_beyond_4gib():
     cols = np.concatenate([cols, np.arange(600) % N, np.arange(256) % N])
     D = p.new_d()
     print("[max] K-contiguous A > 4 GiB", flush=True)
-    migemm.gemm_run(migemm.Plan(p.desc()).handle, p.dA, p.dB, None, D, p.alpha, 0.0)
+    plan = migemm.Plan(p.desc())
+    migemm.gemm_run(plan, p.dA, p.dB, None, D, p.alpha, 0.0)
     torch.cuda.synchronize()
     check_sampled(p, D, rows, cols)
 

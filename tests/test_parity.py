@@ -269,6 +269,31 @@ def test_plan_info_matches_the_persistent_design():
     assert "gfx950" in props.gcnArchName
 
 
+def test_destroyed_plan_is_rejected_before_launch():
+    # A plan handle outlives its Plan object when it is taken from a
+    # temporary (gemm_run(Plan(d).handle, ...)): the C plan is destroyed
+    # before the call starts.  The library must refuse it, not launch with
+    # arguments read from freed memory; D stays as it was.
+    p = Problem.random(torch.Generator().manual_seed(61), 256, 256, 64).to_device()
+    D = p.new_d()
+    with pytest.raises(migemm.MigemmError) as e:
+        migemm.gemm_run(migemm.Plan(p.desc()).handle, p.dA, p.dB, None, D, 1.0, 0.0)
+    assert e.value.status == migemm.MIGEMM_ERR_INVALID_ARG
+    plan = migemm.Plan(p.desc())
+    h = plan.handle
+    assert migemm.gemm_plan_destroy(h) == migemm.MIGEMM_OK
+    assert migemm.gemm_plan_destroy(h) == migemm.MIGEMM_ERR_INVALID_ARG   # not twice
+    assert migemm.gemm_run(h, p.dA, p.dB, None, D, 1.0, 0.0, check=False) == migemm.MIGEMM_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.isnan(D.float()).all()
+    plan.handle = None
+    # A Plan object passed itself stays alive for the call.
+    migemm.gemm_run(migemm.Plan(p.desc()), p.dA, p.dB, None, D, 1.0, 0.0)
+    torch.cuda.synchronize()
+    r = check_full(p, D)
+    assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, r
+
+
 def test_misaligned_pointer_is_rejected_before_launch():
     g = torch.Generator().manual_seed(2)
     p = Problem.random(g, 64, 64, 64).to_device()

@@ -6,7 +6,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <unordered_set>
 
 #include "../../include/migemm.h"
 #include "kernel/params.hpp"
@@ -177,6 +179,23 @@ bool stream_k_pays(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
   return split < whole;
 }
 
+// The plans alive in this process.  Every entry point that takes a plan
+// looks it up here first, so a destroyed plan (or any other pointer that is
+// not a live plan) gives MIGEMM_ERR_INVALID_ARG instead of kernel arguments
+// read from freed memory.  (A new plan created at the address of a destroyed
+// one is that new plan: the check is exact for pointers that were never
+// plans and for destroyed plans whose address has not been reused.)
+std::mutex g_plans_mu;
+std::unordered_set<const migemm_plan*>& live_plans() {
+  static std::unordered_set<const migemm_plan*> s;
+  return s;
+}
+bool plan_is_live(const migemm_plan* p) {
+  if (!p) return false;
+  std::lock_guard<std::mutex> lock(g_plans_mu);
+  return live_plans().count(p) != 0;
+}
+
 bool trace_enabled() {
   const char* e = std::getenv("MIGEMM_TRACE");
   return e && e[0] && e[0] != '0';
@@ -307,17 +326,26 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
                  migemm::kernel_lds_bytes(p->sel), migemm::kStages, p->cu_count,
                  p->sel.stream_k ? a.num_tiles - a.sk_first : 0, p->workspace_bytes);
   }
+  {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    live_plans().insert(p);
+  }
   *out = p;
   return MIGEMM_OK;
 }
 
 int gemm_plan_destroy(migemm_plan* plan) {
+  if (!plan) return MIGEMM_OK;
+  {
+    std::lock_guard<std::mutex> lock(g_plans_mu);
+    if (live_plans().erase(plan) == 0) return MIGEMM_ERR_INVALID_ARG;  // not a live plan
+  }
   delete plan;
   return MIGEMM_OK;
 }
 
 int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
-  if (!p || !out) return MIGEMM_ERR_INVALID_ARG;
+  if (!plan_is_live(p) || !out) return MIGEMM_ERR_INVALID_ARG;
   std::memset(out, 0, sizeof(*out));
   out->tiles_m = p->base.tiles_m;
   out->tiles_n = p->base.tiles_n;
@@ -343,11 +371,11 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
 }
 
 size_t gemm_plan_workspace_size(const migemm_plan* plan) {
-  return plan ? plan->workspace_bytes : 0;
+  return plan_is_live(plan) ? plan->workspace_bytes : 0;
 }
 
 int gemm_workspace_init(const migemm_plan* p, void* workspace, void* stream) {
-  if (!p) return MIGEMM_ERR_INVALID_ARG;
+  if (!plan_is_live(p)) return MIGEMM_ERR_INVALID_ARG;
   if (p->workspace_bytes == 0) return MIGEMM_OK;
   if (!workspace) return MIGEMM_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return MIGEMM_ERR_MISALIGNED;
@@ -365,7 +393,7 @@ int gemm_workspace_init(const migemm_plan* p, void* workspace, void* stream) {
 static int check_run(const migemm_plan* p, const void* A, const void* B, const void* C,
                      const void* D, float beta, bool consumer, const float* row_sum,
                      const float* row_max, const void* D_copy) {
-  if (!p) return MIGEMM_ERR_INVALID_ARG;
+  if (!plan_is_live(p)) return MIGEMM_ERR_INVALID_ARG;
   if (consumer && !(p->desc.flags & MIGEMM_F_TILE_CONSUMER)) return MIGEMM_ERR_INVALID_ARG;
   if (p->M == 0 || p->N == 0) return MIGEMM_OK;
   if (!D || (p->K > 0 && (!A || !B))) return MIGEMM_ERR_INVALID_ARG;
@@ -444,7 +472,7 @@ int gemm_run_with_tile_consumer(const migemm_plan* plan, const void* A, const vo
 
 int gemm_debug_read(const migemm_plan* p, const void* workspace, void* stream,
                     migemm_debug_info* out) {
-  if (!p || !out || !workspace || !p->debug) return MIGEMM_ERR_INVALID_ARG;
+  if (!plan_is_live(p) || !out || !workspace || !p->debug) return MIGEMM_ERR_INVALID_ARG;
   std::memset(out, 0, sizeof(*out));
   uint32_t head[2] = {0, 0};
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess ||

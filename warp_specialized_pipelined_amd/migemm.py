@@ -159,6 +159,15 @@ def _stream(s) -> int | None:
     return int(s)
 
 
+def _plan(plan):
+    """A plan handle from a Plan object or a raw handle.  Passing the Plan
+    object keeps it (and so the C plan) alive for the whole call; a handle
+    taken from a temporary Plan, as in gemm_run(Plan(d).handle, ...), is
+    already destroyed when the call starts, which the library then rejects
+    with MIGEMM_ERR_INVALID_ARG."""
+    return getattr(plan, "handle", plan)
+
+
 def make_desc(M, N, K, a_type, b_type, a_rs, a_cs, b_rs, b_cs, c_rs, c_cs, d_rs, d_cs,
               device=0, flags=0, max_workgroups=0, c_type=MIGEMM_BF16, d_type=MIGEMM_BF16,
               L=1, a_bs=0, b_bs=0, c_bs=0, d_bs=0, debug_wait_ticks=0, debug_force_wait=0):
@@ -185,23 +194,23 @@ def gemm_plan_create(desc: migemm_desc) -> int:
 
 
 def gemm_plan_destroy(plan: int) -> int:
-    return int(load().gemm_plan_destroy(plan))
+    return int(load().gemm_plan_destroy(_plan(plan)))
 
 
 def gemm_plan_get_info(plan: int) -> migemm_plan_info:
     info = migemm_plan_info()
-    st = load().gemm_plan_get_info(plan, ctypes.byref(info))
+    st = load().gemm_plan_get_info(_plan(plan), ctypes.byref(info))
     if st != MIGEMM_OK:
         raise MigemmError(st, "gemm_plan_get_info")
     return info
 
 
 def gemm_plan_workspace_size(plan: int) -> int:
-    return int(load().gemm_plan_workspace_size(plan))
+    return int(load().gemm_plan_workspace_size(_plan(plan)))
 
 
 def gemm_workspace_init(plan, workspace, stream=None, check: bool = True) -> int:
-    st = load().gemm_workspace_init(plan, _ptr(workspace), _stream(stream))
+    st = load().gemm_workspace_init(_plan(plan), _ptr(workspace), _stream(stream))
     if check and st != MIGEMM_OK:
         raise MigemmError(st, "gemm_workspace_init")
     return st
@@ -209,7 +218,7 @@ def gemm_workspace_init(plan, workspace, stream=None, check: bool = True) -> int
 
 def gemm_run(plan, A, B, C, D, alpha: float, beta: float, workspace=None, stream=None,
              check: bool = True) -> int:
-    st = load().gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha), float(beta),
+    st = load().gemm_run(_plan(plan), _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha), float(beta),
                          _ptr(workspace), _stream(stream))
     if check and st != MIGEMM_OK:
         raise MigemmError(st, "gemm_run")
@@ -218,7 +227,7 @@ def gemm_run(plan, A, B, C, D, alpha: float, beta: float, workspace=None, stream
 
 def gemm_run_no_alloc(plan, A, B, C, D, alpha: float, beta: float, stream=None,
                       check: bool = True) -> int:
-    st = load().gemm_run_no_alloc(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha),
+    st = load().gemm_run_no_alloc(_plan(plan), _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha),
                                   float(beta), _stream(stream))
     if check and st != MIGEMM_OK:
         raise MigemmError(st, "gemm_run_no_alloc")
@@ -229,13 +238,13 @@ def gemm_debug_read(plan, workspace, stream=None) -> tuple:
     """(status, migemm_debug_info): synchronizes the stream, reads the debug
     header.  status is MIGEMM_ERR_TIMEOUT when a bounded wait gave up."""
     info = migemm_debug_info()
-    st = load().gemm_debug_read(plan, _ptr(workspace), _stream(stream), ctypes.byref(info))
+    st = load().gemm_debug_read(_plan(plan), _ptr(workspace), _stream(stream), ctypes.byref(info))
     return int(st), info
 
 
 def gemm_run_with_tile_consumer(plan, A, B, C, D, alpha: float, beta: float, row_sum, row_max,
                                 D_copy, workspace=None, stream=None, check: bool = True) -> int:
-    st = load().gemm_run_with_tile_consumer(plan, _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha),
+    st = load().gemm_run_with_tile_consumer(_plan(plan), _ptr(A), _ptr(B), _ptr(C), _ptr(D), float(alpha),
                                             float(beta), _ptr(row_sum), _ptr(row_max),
                                             _ptr(D_copy), _ptr(workspace), _stream(stream))
     if check and st != MIGEMM_OK:
