@@ -49,6 +49,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_c_client(verbose: bool = False) -> str:
+    """Compile tests/c_client.c, a plain C program that uses the C ABI with
+    its own device memory (no Python), against the in-tree library, into
+    tests/_build/c_client.  Needs build() first."""
+    root = os.path.dirname(HERE)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    out_dir = os.path.join(root, "tests", "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    exe = os.path.join(out_dir, "c_client")
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include"),
+           os.path.join(root, "tests", "c_client.c"), "-o", exe + ".tmp",
+           "-L", HERE, "-lmigemm", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../warp_specialized_pipelined_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
 def dump_asm(out_dir: str) -> str:
     """Write the gfx950 assembly of the kernel translation unit to out_dir."""
     os.makedirs(out_dir, exist_ok=True)
