@@ -1,8 +1,11 @@
 """The oracle's pins must catch plausible mistakes in the oracle.
 
-Each case plants one mistake in a copy of oracle/oracle.c (on the CPU),
-builds it, and runs the pin suite (tests/test_oracle.py) against the broken
-build.  The suite must fail for every planted mistake."""
+Each case plants one mistake in a copy of the oracle (on the CPU) -- in
+oracle/oracle.c, built into a library of its own, or in the Python side
+(oracle/__init__.py: the acceptance check, its tolerances and the widening
+of GPU results), imported in place of the real one -- and runs the pin
+suite (tests/test_oracle.py) against it.  The suite must fail for every
+planted mistake."""
 import os
 import subprocess
 import sys
@@ -52,14 +55,9 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(mutation):
-    # (name, old, new[, old2, new2 ...]): every `old` must occur once
-    name, pairs = mutation[0], list(zip(mutation[1::2], mutation[2::2]))
-    src = open(SRC).read()
-    for old, new in pairs:
-        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
-        src = src.replace(old, new)
+def run_pins_with_c_source(src):
+    """Build src as the oracle library and run the pin suite against it;
+    returns pytest's exit status and output."""
     with tempfile.TemporaryDirectory() as d:
         msrc = os.path.join(d, "oracle_mut.c")
         lib = os.path.join(d, "liboracle_mut.so")
@@ -70,4 +68,80 @@ def test_pins_catch_planted_mistake(mutation):
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                             os.path.join(ROOT, "tests", "test_oracle.py")],
                            cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"the pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
+    return r.returncode, r.stdout
+
+
+def test_c_side_harness_passes_the_unchanged_oracle():
+    # The control: the unchanged source, built and loaded the same way,
+    # passes every pin.
+    st, out = run_pins_with_c_source(open(SRC).read())
+    assert st == 0, out[-2000:]
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(mutation):
+    # (name, old, new[, old2, new2 ...]): every `old` must occur once
+    name, pairs = mutation[0], list(zip(mutation[1::2], mutation[2::2]))
+    src = open(SRC).read()
+    for old, new in pairs:
+        assert src.count(old) == 1, f"mutation {name} no longer matches oracle.c"
+        src = src.replace(old, new)
+    st, out = run_pins_with_c_source(src)
+    # 1: tests ran and failed (not a collection or usage error)
+    assert st == 1, f"the pins did not catch mutation {name} (pytest status {st}):\n{out[-2000:]}"
+
+
+# (name, text in oracle/__init__.py, replacement): the Python half of the oracle.
+PY_MUTATIONS = [
+    ("tolerance_bf16_looser", "TOLERANCE = {BF16: (2.0 ** -8, 1e-4)", "TOLERANCE = {BF16: (2.0 ** -7, 1e-4)"),
+    ("tolerance_e4m3_like_bf16", "E4M3: (2.0 ** -7, 2e-3)}", "E4M3: (2.0 ** -8, 2e-3)}"),
+    ("check_ignores_alpha", "coef * abs(float(alpha)) * absum", "coef * absum"),
+    ("check_lets_nan_pass", "bad = ~finite | (err > bound)", "bad = (err > bound)"),
+    ("check_bound_exclusive", "bad = ~finite | (err > bound)", "bad = ~finite | (err >= bound)"),
+    ("check_signed_relative_bound", "bound = rel * np.abs(ref)", "bound = rel * ref"),
+    ("widen_drops_sign", "c = np.asarray(codes).view(np.uint16).astype(np.uint32) << 16",
+     "c = (np.asarray(codes).view(np.uint16).astype(np.uint32) & 0x7FFF) << 16"),
+    ("widen_wrong_half", "c = np.asarray(codes).view(np.uint16).astype(np.uint32) << 16",
+     "c = np.asarray(codes).view(np.uint16).astype(np.uint32) << 15"),
+]
+
+
+def run_pins_with_python_side(src_text):
+    """Run the pin suite with oracle/__init__.py replaced by src_text (in a
+    temporary copy of the package, beside the original oracle.c); returns
+    pytest's exit status and output."""
+    import shutil
+    with tempfile.TemporaryDirectory() as d:
+        pkg = os.path.join(d, "oracle")
+        os.makedirs(pkg)
+        shutil.copy(SRC, os.path.join(pkg, "oracle.c"))
+        open(os.path.join(pkg, "__init__.py"), "w").write(src_text)
+        # The mutated package is imported first, so the pin suite's own
+        # `import oracle` finds it in sys.modules.
+        prog = ("import sys; sys.path.insert(0, %r)\n"
+                "import oracle\n"
+                "assert oracle.__file__.startswith(%r), oracle.__file__\n"
+                "import pytest\n"
+                "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', %r]))\n"
+                % (d, d, os.path.join(ROOT, "tests", "test_oracle.py")))
+        env = {k: v for k, v in os.environ.items() if k != "MIGEMM_ORACLE_LIB"}
+        r = subprocess.run([sys.executable, "-c", prog], cwd=ROOT, env=env, capture_output=True,
+                           text=True, timeout=600)
+    return r.returncode, r.stdout
+
+
+def test_python_side_harness_passes_the_unchanged_oracle():
+    # The control: the same harness on an unchanged copy passes every pin,
+    # so a failure under a mutation is the mutation's doing.
+    st, out = run_pins_with_python_side(open(os.path.join(ROOT, "oracle", "__init__.py")).read())
+    assert st == 0, out[-2000:]
+
+
+@pytest.mark.parametrize("mutation", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_pins_catch_planted_mistake_in_python_side(mutation):
+    name, old, new = mutation
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) == 1, f"mutation {name} no longer matches oracle/__init__.py"
+    st, out = run_pins_with_python_side(src.replace(old, new))
+    # 1: tests ran and failed (not a collection or usage error)
+    assert st == 1, f"the pins did not catch mutation {name} (pytest status {st}):\n{out[-2000:]}"
