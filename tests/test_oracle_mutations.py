@@ -38,6 +38,12 @@ MUTATIONS = [
      "      double r = s;\n      if (beta != 0.0) r += beta * elem(c_type, C, c_rs, c_cs, i, j);\n      ref[i * N + j] = alpha * r;"),
     ("entries_c_transposed", "    if (beta != 0.0) r += beta * elem(c_type, C, c_rs, c_cs, i, j);\n    ref[e] = r;",
      "    if (beta != 0.0) r += beta * elem(c_type, C, c_cs, c_rs, i, j);\n    ref[e] = r;"),
+    ("entries_rows_cols_swapped", "    int64_t i = rows[e], j = cols[e];", "    int64_t i = cols[e], j = rows[e];"),
+    ("entries_drop_last_k", "    for (int64_t k = 0; k < K; ++k) {\n      double p = elem(a_type",
+     "    for (int64_t k = 0; k + 1 < K; ++k) {\n      double p = elem(a_type"),
+    ("entries_absum_signed", "      s += p;\n      t += fabs(p);\n    }\n    double r", "      s += p;\n      t += p;\n    }\n    double r"),
+    ("entries_alpha_dropped", "    double r = alpha * s;\n    if (beta != 0.0) r += beta * elem(c_type, C, c_rs, c_cs, i, j);\n    ref[e] = r;",
+     "    double r = s;\n    if (beta != 0.0) r += beta * elem(c_type, C, c_rs, c_cs, i, j);\n    ref[e] = r;"),
     ("rowsum_in_double", "volatile float s = 0.0f;", "volatile double s = 0.0;"),
     ("rowsum_from_minus_zero", "volatile float s = 0.0f;", "volatile float s = -0.0f;"),
     ("rowsum_descending", "      for (int64_t j = j0; j < j1; ++j) {\n        float v",
