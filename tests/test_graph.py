@@ -84,3 +84,33 @@ def test_graph_tile_consumer(overlap):
     want = [D.clone(), Dc.clone(), rs.clone(), rm.clone()]
     g = capture(call)
     replay_and_check(g, [D, Dc, rs, rm], want, lambda: torch.cuda.synchronize())
+
+
+def test_graph_no_alloc_stream_k():
+    # gemm_run_no_alloc is for callers that cannot allocate, such as code under
+    # graph capture: a stream-K plan takes its workspace from the library's
+    # fixed scratch, and the captured call clears the scratch's counters with
+    # a fill kernel of its own.  Between replays another plan's eager
+    # no-allocation run reuses that scratch; every replay must still give the
+    # eager result.
+    gen = torch.Generator().manual_seed(13)
+    p = Problem.random(gen, 1000, 700, 520, "row", "row", dist="normal", beta=0.5).to_device()
+    q = Problem.random(gen, 600, 520, 300, "row", "col", dist="normal").to_device()
+    sk = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_STREAM_K_FORCE, max_workgroups=6))
+    sk_other = migemm.Plan(q.desc(flags=migemm.MIGEMM_F_STREAM_K_FORCE, max_workgroups=5))
+    assert sk.info.stream_k_tiles > 0 and sk_other.info.stream_k_tiles > 0
+    D, Dq = p.new_d(), q.new_d()
+
+    def call(stream):
+        migemm.gemm_run_no_alloc(sk, p.dA, p.dB, p.dC, D, p.alpha, p.beta, stream)
+
+    call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = [D.clone()]
+    g = capture(call)
+
+    def other_run():
+        migemm.gemm_run_no_alloc(sk_other, q.dA, q.dB, None, Dq, q.alpha, 0.0)
+        torch.cuda.synchronize()
+
+    replay_and_check(g, [D], want, other_run)
