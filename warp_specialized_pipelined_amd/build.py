@@ -4,7 +4,8 @@
     python -m warp_specialized_pipelined_amd.build --asm DIR      # also write the AMD assembly to DIR
 
 The library is written next to this file so that it travels with the source
-tree; nothing is installed.
+tree (objects and the host-sanitizer variant under _build/); nothing is
+installed.
 """
 from __future__ import annotations
 
@@ -38,37 +39,77 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libmigemm.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, *SOURCES]
+OBJ_DIR = os.path.join(HERE, "_build")
+# The host-side sanitizer build of the C ABI layer (api.cpp).  Each
+# -fsanitize= flag follows -Xarch_host, so no device code is instrumented.
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=CSRC)
+
+
+def _obj(name):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    return os.path.join(OBJ_DIR, name)
+
+
+def build(verbose: bool = False, asan: bool = True) -> str:
+    """Compile every HIP source into libmigemm.so (always recompiles): the
+    kernel translation unit once into an object, the C ABI layer, and the
+    link.  With asan, also _build/libmigemm_asan.so: the same kernel object
+    with the C ABI layer built under the host AddressSanitizer."""
+    kobj, aobj = _obj("gemm_kernels.o"), _obj("api.o")
+    _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", kobj, os.path.join(CSRC, "gemm_kernels.hip")], verbose)
+    _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", aobj, os.path.join(CSRC, "api.cpp")], verbose)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, aobj, kobj], verbose)
     os.replace(tmp, LIB)
+    if asan:
+        sobj, slib = _obj("api_asan.o"), _obj("libmigemm_asan.so")
+        _run([hipcc(), *HIPCC_FLAGS, *ASAN_HOST_FLAGS, "-c", "-o", sobj,
+              os.path.join(CSRC, "api.cpp")], verbose)
+        _run([hipcc(), *HIPCC_FLAGS, *ASAN_HOST_FLAGS, "-shared", "-o", slib + ".tmp", sobj, kobj],
+             verbose)
+        os.replace(slib + ".tmp", slib)
     return LIB
 
 
-def build_c_client(verbose: bool = False) -> str:
+def build_c_client(verbose: bool = False) -> list:
     """Compile tests/c_client.c, a plain C program that uses the C ABI with
-    its own device memory (no Python), against the in-tree library, into
-    tests/_build/c_client.  Needs build() first."""
+    its own device memory (no Python), into tests/_build/c_client against
+    the in-tree library, and into tests/_build/c_client_asan, under the
+    host AddressSanitizer, against _build/libmigemm_asan.so when build()
+    made it.  Needs build() first."""
     root = os.path.dirname(HERE)
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     out_dir = os.path.join(root, "tests", "_build")
     os.makedirs(out_dir, exist_ok=True)
-    exe = os.path.join(out_dir, "c_client")
-    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__",
-           "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include"),
-           os.path.join(root, "tests", "c_client.c"), "-o", exe + ".tmp",
-           "-L", HERE, "-lmigemm", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
-           "-Wl,-rpath,$ORIGIN/../../warp_specialized_pipelined_amd",
-           "-Wl,-rpath," + os.path.join(rocm, "lib")]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(exe + ".tmp", exe)
-    return exe
+    common = ["-std=c11", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__",
+              "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include"),
+              os.path.join(root, "tests", "c_client.c")]
+    hip = ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    built = []
+    variants = [("c_client", "gcc", [], HERE, "migemm",
+                 "$ORIGIN/../../warp_specialized_pipelined_amd")]
+    if os.path.exists(os.path.join(OBJ_DIR, "libmigemm_asan.so")):
+        # The sanitized library comes from hipcc's clang, so the client is
+        # built by ROCm's clang too: one sanitizer runtime, clang's.
+        variants.append(("c_client_asan", os.path.join(rocm, "llvm", "bin", "clang"),
+                         ["-fsanitize=address", "-fno-omit-frame-pointer"], OBJ_DIR, "migemm_asan",
+                         "$ORIGIN/../../warp_specialized_pipelined_amd/_build"))
+    for name, cc, extra, libdir, lib, rpath in variants:
+        exe = os.path.join(out_dir, name)
+        cmd = [cc, *extra, *common, "-o", exe + ".tmp", "-L", libdir, "-l" + lib,
+               "-Wl,-rpath," + rpath, *hip]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(exe + ".tmp", exe)
+        built.append(exe)
+    return built
 
 
 def dump_asm(out_dir: str) -> str:
