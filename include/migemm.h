@@ -198,8 +198,11 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out);
 
 /* Free a plan (NULL is accepted and does nothing).  A pointer that is not a
  * live plan (destroyed already, or never created) gives INVALID_ARG and
- * frees nothing.  Host memory only; the pages have no counterpart (their
- * Params live in the caller's object). */
+ * frees nothing.  Destroying a plan while another thread is inside a call
+ * on it is the caller's error (the liveness check catches stale handles,
+ * not such races); runs already enqueued do not need the plan.  Host
+ * memory only; the pages have no counterpart (their Params live in the
+ * caller's object). */
 int gemm_plan_destroy(migemm_plan* plan);
 
 /* Copy the plan's choices into *out (grid, block, tiles, ring depths).

@@ -185,10 +185,12 @@ bool stream_k_pays(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
 // read from freed memory.  (A new plan created at the address of a destroyed
 // one is that new plan: the check is exact for pointers that were never
 // plans and for destroyed plans whose address has not been reused.)
+// (The set is never freed, so a plan destroyed while the process exits --
+// after static destructors have run -- still finds it.)
 std::mutex g_plans_mu;
 std::unordered_set<const migemm_plan*>& live_plans() {
-  static std::unordered_set<const migemm_plan*> s;
-  return s;
+  static std::unordered_set<const migemm_plan*>* s = new std::unordered_set<const migemm_plan*>();
+  return *s;
 }
 bool plan_is_live(const migemm_plan* p) {
   if (!p) return false;
