@@ -129,6 +129,8 @@ typedef enum migemm_status {
  *     major); a column-major D is computed as D^T = B^T A^T;
  *   - the tile-consumer flag requires a row-major D;
  *   - the byte span of 256 rows (or K rows) of an operand fits in 2^31;
+ *   - each operand, with all its batches, spans at most 2^47 bytes (else
+ *     UNSUPPORTED; this also rejects strides whose products would wrap);
  *   - batches (the pages' rank-4 problem shape, L appended to MNK): L = 0 or
  *     1 is one product; for L > 1 matrix l of X starts x_bs * l elements
  *     after X, every x_bs >= 0 and x_bs times the element size a multiple of

@@ -151,6 +151,16 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(debug_wait_ticks=1000), migemm.MIGEMM_ERR_INVALID_ARG),                   # needs the flag
     (dict(flags=migemm.MIGEMM_F_HANDOFF_DEBUG | migemm.MIGEMM_F_TILE_CONSUMER,
           debug_force_wait=-1), migemm.MIGEMM_ERR_INVALID_ARG),
+    # strides whose products would wrap a 64-bit integer: each operand's span
+    # (with its batches) is bounded at 2^47 bytes, exactly
+    (dict(a_rs=1 << 62), migemm.MIGEMM_ERR_UNSUPPORTED),
+    (dict(a_rs=1 << 59), migemm.MIGEMM_ERR_UNSUPPORTED),
+    (dict(b_rs=1 << 61), migemm.MIGEMM_ERR_UNSUPPORTED),
+    (dict(d_rs=1 << 60, c_rs=1 << 60), migemm.MIGEMM_ERR_UNSUPPORTED),
+    # column-major A with a 2^24-byte leading stride (64 K rows span 2^30):
+    # K = 2^23 puts it just below 2^47 bytes, K = 2^23 + 2 just past
+    (dict(K=1 << 23, a_rs=1, a_cs=1 << 23), migemm.MIGEMM_OK),
+    (dict(K=(1 << 23) + 2, a_rs=1, a_cs=1 << 23), migemm.MIGEMM_ERR_UNSUPPORTED),
     (dict(K=5001, a_rs=5008), migemm.MIGEMM_OK),                            # K-contiguous A, any K
     (dict(K=5001, a_rs=5001), migemm.MIGEMM_ERR_MISALIGNED),                # but 16-byte rows
 ])
@@ -167,6 +177,8 @@ def test_validation_status_codes(over, status):
     (dict(L=2, a_bs=4, d_bs=4000 * 3000), migemm.MIGEMM_ERR_MISALIGNED),     # 8-byte batch step
     (dict(L=2, d_bs=4000 * 3000 + 4), migemm.MIGEMM_ERR_MISALIGNED),
     (dict(L=1 << 24, d_bs=4000 * 3000), migemm.MIGEMM_ERR_UNSUPPORTED),      # 2^31+ tiles
+    (dict(L=3, a_bs=1 << 61, d_bs=4000 * 3000), migemm.MIGEMM_ERR_UNSUPPORTED),  # wrapping batch step
+    (dict(L=2, a_bs=(1 << 46) // 2, d_bs=4000 * 3000), migemm.MIGEMM_OK),   # 64 TiB step: in range
 ])
 def test_batch_validation(over, status):
     assert migemm.gemm_desc_validate(desc_for(W, **over)) == status

@@ -65,6 +65,23 @@ int64_t extent_bytes(int64_t rows, int64_t cols, int64_t rs, int64_t cs, int es)
 
 int elem_size(int32_t t) { return t == MIGEMM_BF16 ? 2 : (t == MIGEMM_FP8_E4M3 ? 1 : 0); }
 
+// The bytes one operand may span -- its first batch matrix, and its last
+// batch matrix from the first -- computed exactly (128-bit), must stay
+// within 2^47 (128 TiB, beyond any device's memory).  Every later product of
+// sizes and strides, here and in the kernels' 64-bit address arithmetic,
+// then stays far from overflow; without this bound a huge stride could wrap
+// a product past the other checks and put a buffer base outside any
+// allocation.
+constexpr __int128 kMaxOperandBytes = (__int128)1 << 47;
+bool span_in_range(int64_t rows, int64_t cols, int64_t rs, int64_t cs, int es, int64_t L,
+                   int64_t bs) {
+  if (rows <= 0 || cols <= 0) return true;
+  const __int128 one = ((__int128)(rows - 1) * rs + (__int128)(cols - 1) * cs + 1) * es;
+  const __int128 batches = (__int128)(L - 1) * bs * es;
+  return one <= kMaxOperandBytes && batches <= kMaxOperandBytes &&
+         one + batches <= kMaxOperandBytes;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxRsrcSpan = 0x7FFFFFF0 - 1024;
@@ -105,6 +122,15 @@ int validate(const migemm_desc* d, Canon* out) {
   if (!orient(d->M, d->K, d->a_rs, d->a_cs, &oa) || !orient(d->K, d->N, d->b_rs, d->b_cs, &ob) ||
       !orient(d->M, d->N, d->c_rs, d->c_cs, &oc) || !orient(d->M, d->N, d->d_rs, d->d_cs, &od))
     return MIGEMM_ERR_INVALID_ARG;
+  {
+    const int64_t Lc = d->L > 1 ? d->L : 1;
+    const bool b = Lc > 1;
+    if (!span_in_range(d->M, d->K, d->a_rs, d->a_cs, es, Lc, b ? d->a_bs : 0) ||
+        !span_in_range(d->K, d->N, d->b_rs, d->b_cs, es, Lc, b ? d->b_bs : 0) ||
+        !span_in_range(d->M, d->N, d->c_rs, d->c_cs, 2, Lc, b ? d->c_bs : 0) ||
+        !span_in_range(d->M, d->N, d->d_rs, d->d_cs, 2, Lc, b ? d->d_bs : 0))
+      return MIGEMM_ERR_UNSUPPORTED;
+  }
   if (oc.row_major != od.row_major) return MIGEMM_ERR_UNSUPPORTED;
   if ((d->flags & MIGEMM_F_TILE_CONSUMER) && !od.row_major) return MIGEMM_ERR_UNSUPPORTED;
   // 16-byte rows for every operand.
