@@ -283,3 +283,69 @@ def test_header_constants_match_the_binding():
     assert "MIGEMM_F_CONSUMER_OVERLAP" in defines and len(defines) >= 6
     for name, value in defines.items():
         assert getattr(migemm, name) == int(value, 0), name
+
+
+def test_validation_accepts_only_addressable_descriptions():
+    """Property: for descriptions with sizes and strides anywhere in int64
+    (hypothesis explores the extremes), gemm_desc_validate never crashes,
+    and whatever it accepts keeps every operand -- with all its batches --
+    within 2^47 bytes, its leading strides 16-byte aligned, and the 32-bit
+    offsets of one tile band (256 rows, or one 128-byte stage of K rows)
+    below 2^31.  The model uses Python's exact integers, not the library's
+    arithmetic.  Leading strides are drawn as the contiguous extent plus an
+    extra, rounded up to 16 bytes, so that most descriptions are valid and
+    the bounds, not the alignment rule, decide."""
+    from hypothesis import HealthCheck, given, settings, strategies as st
+
+    size = st.one_of(st.integers(0, 3000), st.integers(0, 1 << 20),
+                     st.sampled_from([0, 1, 255, 256, 257, 1 << 23, (1 << 23) + 2, 1 << 30, 1 << 40,
+                                      (1 << 62) + 3, (1 << 63) - 1]))
+    extra = st.one_of(st.just(0), st.integers(0, 1 << 16),
+                      st.sampled_from([1 << 20, 1 << 23, 1 << 30, 1 << 40, 1 << 46, 1 << 47,
+                                       1 << 59, 1 << 62]))
+    layout = st.sampled_from(["row", "col"])
+    accepted = []
+
+    def up(x, a):
+        return min(-(-x // a) * a, (1 << 63) - a)
+
+    @settings(max_examples=3000, deadline=None, suppress_health_check=list(HealthCheck))
+    @given(M=size, N=size, K=size, la=layout, lb=layout, xa=extra, xb=extra, xd=extra,
+           fp8=st.booleans(), L=st.one_of(st.just(1), st.integers(2, 8), st.just(1 << 20)),
+           xabs=extra, xbbs=extra, xdbs=extra)
+    def check(M, N, K, la, lb, xa, xb, xd, fp8, L, xabs, xbbs, xdbs):
+        t = migemm.MIGEMM_FP8_E4M3 if fp8 else migemm.MIGEMM_BF16
+        es = 1 if fp8 else 2
+        al = 16 // es
+        lda = up((K if la == "row" else M) + xa, al)
+        ldb = up((N if lb == "row" else K) + xb, al)
+        ldd = up(N + xd, 8)
+        a_rs, a_cs = (lda, 1) if la == "row" else (1, lda)
+        b_rs, b_cs = (ldb, 1) if lb == "row" else (1, ldb)
+        abs_ = up(M * K + xabs, al) if L > 1 else 0
+        bbs = up(K * N + xbbs, al) if L > 1 else 0
+        dbs = up(M * ldd + xdbs, 8) if L > 1 else 0
+        d = migemm.make_desc(M, N, K, t, t, a_rs, a_cs, b_rs, b_cs, ldd, 1, ldd, 1, L=L,
+                             a_bs=abs_, b_bs=bbs, c_bs=dbs, d_bs=dbs)
+        if migemm.gemm_desc_validate(d) != migemm.MIGEMM_OK:
+            return
+        accepted.append((M, N, K))
+        Lc = L if L > 1 else 1
+
+        def span(rows, cols, rs, cs, e, bs):
+            if rows <= 0 or cols <= 0:
+                return 0
+            return ((rows - 1) * rs + (cols - 1) * cs + 1) * e + (Lc - 1) * bs * e
+
+        assert span(M, K, a_rs, a_cs, es, abs_) <= 1 << 47
+        assert span(K, N, b_rs, b_cs, es, bbs) <= 1 << 47
+        assert span(M, N, ldd, 1, 2, dbs) <= 1 << 47
+        for rows_or_cols, ld, kmajor in ((M, lda, la == "row"), (N, ldb, lb == "col")):
+            if rows_or_cols > 0 and K > 0:
+                assert (ld * es) % 16 == 0
+                assert (256 if kmajor else 128 // es) * ld * es < 1 << 31
+        if M > 0 and N > 0:
+            assert (ldd * 2) % 16 == 0 and 256 * ldd * 2 < 1 << 31
+
+    check()
+    assert len(accepted) > 500, len(accepted)   # the property was tested, not vacuous

@@ -72,14 +72,23 @@ int elem_size(int32_t t) { return t == MIGEMM_BF16 ? 2 : (t == MIGEMM_FP8_E4M3 ?
 // then stays far from overflow; without this bound a huge stride could wrap
 // a product past the other checks and put a buffer base outside any
 // allocation.
-constexpr __int128 kMaxOperandBytes = (__int128)1 << 47;
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 47;
 bool span_in_range(int64_t rows, int64_t cols, int64_t rs, int64_t cs, int es, int64_t L,
                    int64_t bs) {
   if (rows <= 0 || cols <= 0) return true;
-  const __int128 one = ((__int128)(rows - 1) * rs + (__int128)(cols - 1) * cs + 1) * es;
-  const __int128 batches = (__int128)(L - 1) * bs * es;
-  return one <= kMaxOperandBytes && batches <= kMaxOperandBytes &&
-         one + batches <= kMaxOperandBytes;
+  // (Called after the orientation check: the strides of a dimension longer
+  // than 1 are at least 1.)  A factor beyond 2^47 alone puts the span past
+  // the bound, so the products below only ever see factors up to 2^47.
+  constexpr int64_t lim = kMaxOperandBytes;
+  if ((rows > 1 && (rows - 1 > lim || rs > lim)) || (cols > 1 && (cols - 1 > lim || cs > lim)))
+    return false;
+  __int128 bytes = ((__int128)(rows - 1) * (rows > 1 ? rs : 0) +
+                    (__int128)(cols - 1) * (cols > 1 ? cs : 0) + 1) * es;
+  if (L > 1 && bs > 0) {  // (a negative batch stride is refused later)
+    if (L - 1 > lim || bs > lim) return false;
+    bytes += (__int128)(L - 1) * bs * es;
+  }
+  return bytes <= kMaxOperandBytes;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -100,6 +109,10 @@ int validate(const migemm_desc* d, Canon* out) {
   if (d->M < 0 || d->N < 0 || d->K < 0 || d->reserved != 0 || d->max_workgroups < 0 ||
       d->reserved2 != 0 || d->debug_wait_ticks < 0 || d->debug_force_wait < 0)
     return MIGEMM_ERR_INVALID_ARG;
+  // No dimension beyond 2^47 (even of an empty product): keeps tile counts
+  // and every size product below from overflowing.
+  if (d->M > kMaxOperandBytes || d->N > kMaxOperandBytes || d->K > kMaxOperandBytes)
+    return MIGEMM_ERR_UNSUPPORTED;
   constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
   if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | MIGEMM_F_HANDOFF_DEBUG |
                     MIGEMM_F_C_IN_EPILOGUE | kStreamK)) != 0)
@@ -134,8 +147,10 @@ int validate(const migemm_desc* d, Canon* out) {
   if (oc.row_major != od.row_major) return MIGEMM_ERR_UNSUPPORTED;
   if ((d->flags & MIGEMM_F_TILE_CONSUMER) && !od.row_major) return MIGEMM_ERR_UNSUPPORTED;
   // 16-byte rows for every operand.
-  if ((oa.ld * es) % 16 || (ob.ld * es) % 16 || (oc.ld * 2) % 16 || (od.ld * 2) % 16)
-    return MIGEMM_ERR_MISALIGNED;
+  // (Written without products: a leading stride may be huge where the other
+  // dimension is 1.)
+  const int64_t per16 = 16 / es;  // elements per 16 bytes
+  if (oa.ld % per16 || ob.ld % per16 || oc.ld % 8 || od.ld % 8) return MIGEMM_ERR_MISALIGNED;
   // Batches: non-negative strides keeping every matrix 16-byte aligned; the
   // batches of D must not overlap (A, B and C may be shared).
   if (d->L < 0) return MIGEMM_ERR_INVALID_ARG;
@@ -146,8 +161,7 @@ int validate(const migemm_desc* d, Canon* out) {
     if (a_bs < 0 || b_bs < 0 || c_bs < 0 || d_bs < 0) return MIGEMM_ERR_INVALID_ARG;
     if (d->M > 0 && d->N > 0 && d_bs * 2 < extent_bytes(d->M, d->N, d->d_rs, d->d_cs, 2))
       return MIGEMM_ERR_INVALID_ARG;
-    if ((a_bs * es) % 16 || (b_bs * es) % 16 || (c_bs * 2) % 16 || (d_bs * 2) % 16)
-      return MIGEMM_ERR_MISALIGNED;
+    if (a_bs % per16 || b_bs % per16 || c_bs % 8 || d_bs % 8) return MIGEMM_ERR_MISALIGNED;
   }
 
   Canon c;
@@ -167,12 +181,14 @@ int validate(const migemm_desc* d, Canon* out) {
   orient(c.M, c.K, c.a_rs, c.a_cs, &ca);
   orient(c.K, c.N, c.b_rs, c.b_cs, &cb);
   const bool ca_k = ca.row_major, cb_k = !cb.row_major;
-  const int64_t span_a = (ca_k ? migemm::kTileM : bk) * ca.ld * es;
-  const int64_t span_b = (cb_k ? migemm::kTileN : bk) * cb.ld * es;
+  // (128-bit products: a leading stride may be anything where the other
+  // dimension is 1, and must not wrap past the bound.)
+  const __int128 span_a = (__int128)(ca_k ? migemm::kTileM : bk) * ca.ld * es;
+  const __int128 span_b = (__int128)(cb_k ? migemm::kTileN : bk) * cb.ld * es;
   if (span_a > kMaxRsrcSpan || span_b > kMaxRsrcSpan) return MIGEMM_ERR_UNSUPPORTED;
   // The epilogue addresses a 256-row band of C and D with 32-bit offsets too.
-  if ((int64_t)migemm::kTileM * c.c_rs * 2 > kMaxRsrcSpan ||
-      (int64_t)migemm::kTileM * c.d_rs * 2 > kMaxRsrcSpan)
+  if ((__int128)migemm::kTileM * c.c_rs * 2 > kMaxRsrcSpan ||
+      (__int128)migemm::kTileM * c.d_rs * 2 > kMaxRsrcSpan)
     return MIGEMM_ERR_UNSUPPORTED;
   if (c.M / migemm::kTileM >= (1 << 20) || c.N / migemm::kTileN >= (1 << 20))
     return MIGEMM_ERR_UNSUPPORTED;
