@@ -349,3 +349,25 @@ def test_validation_accepts_only_addressable_descriptions():
 
     check()
     assert len(accepted) > 500, len(accepted)   # the property was tested, not vacuous
+
+
+def test_validation_under_host_sanitizers():
+    """tests/c_validate_extremes.c runs gemm_desc_validate over ~375,000
+    descriptions with sizes and strides from 0 to 2^63 - 1 (and the
+    plan-taking entry points on pointers that are not plans) against the
+    library built with the host address and undefined-behaviour sanitizers:
+    any signed overflow, bad shift or out-of-bounds access aborts it with a
+    report.  (The validation before its span bounds overflowed here.)"""
+    exe = os.path.join(ROOT, "tests", "_build", "c_validate_extremes")
+    asan_lib = os.path.join(ROOT, "warp_specialized_pipelined_amd", "_build", "libmigemm_asan.so")
+    if not os.path.exists(exe):
+        if not os.path.exists(asan_lib):
+            pytest.skip("the sanitized library is built by __graft_entry__.build()")
+        from warp_specialized_pipelined_amd import build
+        build.build_c_client()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert "runtime error" not in r.stderr and "Sanitizer" not in r.stderr, r.stderr[-3000:]
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr[-2000:])
+    tried, accepted = map(int, re.findall(r"tried (\d+) accepted (\d+)", r.stdout)[0])
+    assert tried > 300000 and accepted > 1000, r.stdout

@@ -40,9 +40,12 @@ def hipcc() -> str:
 
 
 OBJ_DIR = os.path.join(HERE, "_build")
-# The host-side sanitizer build of the C ABI layer (api.cpp).  Each
-# -fsanitize= flag follows -Xarch_host, so no device code is instrumented.
-ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+# The host-side sanitizer build of the C ABI layer (api.cpp): the address
+# and undefined-behaviour sanitizers, any report fatal.  Each -fsanitize=
+# flag follows -Xarch_host, so no device code is instrumented.
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _run(cmd, verbose):
@@ -78,31 +81,36 @@ def build(verbose: bool = False, asan: bool = True) -> str:
 
 
 def build_c_client(verbose: bool = False) -> list:
-    """Compile tests/c_client.c, a plain C program that uses the C ABI with
-    its own device memory (no Python), into tests/_build/c_client against
-    the in-tree library, and into tests/_build/c_client_asan, under the
-    host AddressSanitizer, against _build/libmigemm_asan.so when build()
-    made it.  Needs build() first."""
+    """Compile the C programs of the tests into tests/_build: c_client (the
+    C ABI used from plain C with its own device memory, no Python) against
+    the in-tree library; and, when build() made _build/libmigemm_asan.so,
+    c_client_asan and c_validate_extremes against it, under the host
+    address and undefined-behaviour sanitizers.  Needs build() first."""
     root = os.path.dirname(HERE)
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     out_dir = os.path.join(root, "tests", "_build")
     os.makedirs(out_dir, exist_ok=True)
     common = ["-std=c11", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__",
-              "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include"),
-              os.path.join(root, "tests", "c_client.c")]
+              "-I", os.path.join(root, "include"), "-I", os.path.join(rocm, "include")]
     hip = ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
     built = []
     variants = [("c_client", "gcc", [], HERE, "migemm",
                  "$ORIGIN/../../warp_specialized_pipelined_amd")]
     if os.path.exists(os.path.join(OBJ_DIR, "libmigemm_asan.so")):
-        # The sanitized library comes from hipcc's clang, so the client is
-        # built by ROCm's clang too: one sanitizer runtime, clang's.
-        variants.append(("c_client_asan", os.path.join(rocm, "llvm", "bin", "clang"),
-                         ["-fsanitize=address", "-fno-omit-frame-pointer"], OBJ_DIR, "migemm_asan",
-                         "$ORIGIN/../../warp_specialized_pipelined_amd/_build"))
-    for name, cc, extra, libdir, lib, rpath in variants:
+        # The sanitized library comes from hipcc's clang, so these programs
+        # are built by ROCm's clang too: one sanitizer runtime, clang's.
+        clang = os.path.join(rocm, "llvm", "bin", "clang")
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer"]
+        rp = "$ORIGIN/../../warp_specialized_pipelined_amd/_build"
+        variants.append(("c_client_asan", clang, san, OBJ_DIR, "migemm_asan", rp))
+        variants.append(("c_validate_extremes", clang, san, OBJ_DIR, "migemm_asan", rp,
+                         os.path.join(root, "tests", "c_validate_extremes.c")))
+    for v in variants:
+        name, cc, extra, libdir, lib, rpath = v[:6]
+        src = v[6] if len(v) > 6 else os.path.join(root, "tests", "c_client.c")
         exe = os.path.join(out_dir, name)
-        cmd = [cc, *extra, *common, "-o", exe + ".tmp", "-L", libdir, "-l" + lib,
+        cmd = [cc, *extra, *common, src, "-o", exe + ".tmp", "-L", libdir, "-l" + lib,
                "-Wl,-rpath," + rpath, *hip]
         if verbose:
             print(" ".join(cmd), flush=True)
