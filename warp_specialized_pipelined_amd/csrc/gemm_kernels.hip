@@ -102,8 +102,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
       trace_event(n, wave, kEvLoopEnd, lane);
-      const int s = n % kHandoffSlots;
-      HandoffRing::acquire(s, n / kHandoffSlots, lane);
+      const int s = handoff_slot(n);
+      HandoffRing::acquire(s, handoff_use(n), lane);
       trace_event(n, wave, kEvAcquired, lane);
       const LaneIds ie(lane, wave);
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       trace_put(rec, kEvCommitted, now_ticks(), lane);
       trace_put(rec, kTrOccupancy, occ, lane);
       trace_put(rec, kTrTileId, (uint64_t)L, lane);
-      cons.begin(a, s, n / kHandoffSlots, n, wave, lane);
+      cons.begin(a, s, handoff_use(n), n, wave, lane);
       cons.fold_staged(wave, lane);
       cons.copy_staged(wave, lane);
       wait_lgkmcnt<0>();  // staging reads done ...
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       const LaneIds id(lane, wave);
       mainloop<ES, AK, BK>(acc, ab, t.tm, t.tn, id.wave, id.lane, cons);
       trace_event(n, wave, kEvLoopEnd, lane);
-      const int s = n % kHandoffSlots;
-      HandoffRing::acquire(s, n / kHandoffSlots, lane);
+      const int s = handoff_slot(n);
+      HandoffRing::acquire(s, handoff_use(n), lane);
       trace_event(n, wave, kEvAcquired, lane);
       const LaneIds ie(lane, wave);
       epilogue_store(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
       trace_put(rec, kTrOccupancy, occ, lane);
       trace_put(rec, kTrTileId, (uint64_t)L, lane);
       cons.drain(wave, lane);  // tile n-1: steps the K loop left, and its release
-      cons.begin(a, s, n / kHandoffSlots, n, wave, lane);
+      cons.begin(a, s, handoff_use(n), n, wave, lane);
       cons.fold_staged(wave, lane);
       wait_lgkmcnt<0>();
       barrier();

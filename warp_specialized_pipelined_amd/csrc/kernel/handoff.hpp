@@ -57,6 +57,7 @@
 #pragma once
 
 #include "gfx950.hpp"
+#include "handoff_rules.hpp"
 #include "params.hpp"
 #include "mainloop.hpp"
 #include "scheduler.hpp"
@@ -171,7 +172,7 @@ struct HandoffRing {
   }
   // Producer side.
   __device__ __forceinline__ static void acquire(int slot, uint32_t use, int lane) {
-    spin_until(word(slot, kEmpty), use * kWaves + handoff_debug().force, lane);
+    spin_until(word(slot, kEmpty), handoff_acquire_target(use) + handoff_debug().force, lane);
   }
   // Publishes the caller's stores of the tile: the workgroup-scope release
   // fence orders them before the count.  (The waves of a workgroup share
@@ -192,14 +193,14 @@ struct HandoffRing {
     uint32_t occ = 0;
 #pragma unroll
     for (int s = 0; s < kHandoffSlots; ++s)
-      occ += load(word(s, kFull)) / kWaves - load(word(s, kEmpty)) / kWaves;
+      occ += handoff_slot_occupancy(load(word(s, kFull)), load(word(s, kEmpty)));
     if (lane == 0) __hip_atomic_fetch_max(dbg + 1, occ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return occ;
   }
   // Consumer side.  Returns the committed tile's id; the acquire fence keeps
   // the consumer's reads of the tile after the observed commit.
   __device__ __forceinline__ static int wait(int slot, uint32_t use, int lane) {
-    spin_until(word(slot, kFull), (use + 1) * kWaves, lane);
+    spin_until(word(slot, kFull), handoff_wait_target(use), lane);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return (int)load(word(slot, kTileId));
   }
