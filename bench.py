@@ -526,6 +526,7 @@ def main():
             if wc.M * wc.N * wc.K <= 256 ** 3:
                 n_c = 200                         # a few microseconds each
             configs[wc.name] = config_figures(wc, per_launch_ms(fn, n_c, stream))
+            configs[wc.name]["tile_m"] = int(plan_c.info.tile_m)   # the plan's tile height
             if wc.dtype == synth.E4M3:
                 clock_extras("fp8_gemm_", fn, statistics.median(per_launch_ms(fn, 5, stream)),
                              wc.flops, 8192)
@@ -565,15 +566,17 @@ def main():
         extra["fp8_gemm_frac_of_peak"] = configs[w8.name]["frac_of_mfma_peak"]
 
         # One GPU's share of an 8-way split of N, 8192 x 1024 x 8192 bf16: 128
-        # tiles on 256 compute units, whole tiles against the stream-K plan;
-        # and 2048 x 2048 x 8192 (64 tiles, each split four ways).
+        # tiles on 256 compute units, whole 256-row tiles against 192-row
+        # tiles (172 of them) and the plan that may choose stream-K; and
+        # 2048 x 2048 x 8192 (64 tiles, each split four ways).
         for (M_, N_, K_, seed, key) in ((8192, 1024, 8192, 81, "share_8192x1024x8192"),
                                         (2048, 2048, 8192, 82, "gemm_2048x2048x8192")):
             log(f"[bench] drawing inputs for {M_}x{N_}x{K_}")
             g = torch.Generator().manual_seed(seed)
             ps = Problem.random(g, M_, N_, K_, "row", "row", dist="normal").to_device()
             Ds = ps.new_d(0.0)
-            plan_w = migemm.Plan(ps.desc())
+            plan_w = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_TILE_M256))
+            plan_t = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_TILE_M192))
             plan_s = migemm.Plan(ps.desc(flags=migemm.MIGEMM_F_STREAM_K))
             ws = None
             if plan_s.workspace_size:
@@ -584,13 +587,19 @@ def main():
                                          stream)
             fs = lambda: migemm.gemm_run(plan_s.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0, ws,
                                          stream)
+            ft = lambda: migemm.gemm_run(plan_t.handle, ps.dA, ps.dB, None, Ds, 1.0, 0.0, None,
+                                         stream)
             settle(fw, stream, 0.2)
             ms_w = statistics.median(per_launch_ms(fw, max(20, args.steps), stream))
+            settle(ft, stream, 0.2)
+            ms_t = statistics.median(per_launch_ms(ft, max(20, args.steps), stream))
             settle(fs, stream, 0.2)
             ms_s = statistics.median(per_launch_ms(fs, max(20, args.steps), stream))
             extra[key + "_whole_tiles_tflops"] = round(flops_s / (ms_w * 1e-3) / 1e12, 1)
+            extra[key + "_tile_m192_tflops"] = round(flops_s / (ms_t * 1e-3) / 1e12, 1)
             extra[key + "_stream_k_tflops"] = round(flops_s / (ms_s * 1e-3) / 1e12, 1)
             extra[key + "_stream_k_tiles"] = int(plan_s.info.stream_k_tiles)
+            extra[key + "_stream_k_plan_tile_m"] = int(plan_s.info.tile_m)
             del ps, Ds, ws
 
     out = {

@@ -108,8 +108,25 @@ typedef enum migemm_status {
  * consumer always reads C in the epilogue.  gemm_plan_get_info reports the
  * choice (c_in_k_loop).  Same results bit for bit either way. */
 #define MIGEMM_F_C_IN_EPILOGUE 0x20u
+/* Output tile height (the kernel page's tile shape, a compile-time choice
+ * there; here two kernels).  Plans take 256 x 256 tiles, except that a
+ * bf16 plan without MIGEMM_F_TILE_CONSUMER may take 192 x 256 tiles where
+ * that gives each persistent workgroup less work: with T tiles on G
+ * workgroups the work is ceil(T / G) tiles, and a 192-row tile takes about
+ * 0.8 of a 256-row one's time (3/4 of the flops at a slightly lower rate),
+ * so a problem whose 256-row tiles leave a poorly filled last round (8192 x
+ * 1024: 128 tiles on 256 compute units) runs 4/3 as many smaller tiles in
+ * one round.  With MIGEMM_F_STREAM_K the plan compares against stream-K too.  MIGEMM_F_TILE_M256 keeps 256 rows;
+ * MIGEMM_F_TILE_M192 forces 192 (bf16 only, else UNSUPPORTED; INVALID_ARG
+ * with MIGEMM_F_TILE_M256, MIGEMM_F_TILE_CONSUMER or a stream-K flag).  A
+ * 192-row plan reads C (beta != 0) in the epilogue.  gemm_plan_get_info
+ * reports the choice (tile_m, tiles_m).  Same results bit for bit either
+ * way: each output's sum runs over K in the same order. */
+#define MIGEMM_F_TILE_M256 0x40u
+#define MIGEMM_F_TILE_M192 0x80u
 
-/* Output tile of the persistent scheduler (and the hand-off unit). */
+/* Output tile of the persistent scheduler (and the hand-off unit); a plan
+ * may report tile_m 192 instead (MIGEMM_F_TILE_M192). */
 #define MIGEMM_TILE_M 256
 #define MIGEMM_TILE_N 256
 

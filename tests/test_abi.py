@@ -132,7 +132,18 @@ W = synth.WORKLOADS[2]  # 4000 x 3000 x 5000, row/row
     (dict(c_rs=1, c_cs=4000), migemm.MIGEMM_ERR_UNSUPPORTED),               # C col, D row
     (dict(flags=migemm.MIGEMM_F_TILE_CONSUMER, c_rs=1, c_cs=4000, d_rs=1, d_cs=4000),
      migemm.MIGEMM_ERR_UNSUPPORTED),                                        # consumer needs row D
-    (dict(flags=0x80), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=0x100), migemm.MIGEMM_ERR_INVALID_ARG),                    # unknown flag
+    (dict(flags=migemm.MIGEMM_F_TILE_M192), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_TILE_M256), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_TILE_M256 | migemm.MIGEMM_F_TILE_CONSUMER), migemm.MIGEMM_OK),
+    (dict(flags=migemm.MIGEMM_F_TILE_M192 | migemm.MIGEMM_F_TILE_M256), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=migemm.MIGEMM_F_TILE_M192 | migemm.MIGEMM_F_TILE_CONSUMER),
+     migemm.MIGEMM_ERR_INVALID_ARG),                                        # 192 rows: no consumer
+    (dict(flags=migemm.MIGEMM_F_TILE_M192 | migemm.MIGEMM_F_STREAM_K), migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=migemm.MIGEMM_F_TILE_M192 | migemm.MIGEMM_F_STREAM_K_FORCE),
+     migemm.MIGEMM_ERR_INVALID_ARG),
+    (dict(flags=migemm.MIGEMM_F_TILE_M192, a_type=migemm.MIGEMM_FP8_E4M3, b_type=migemm.MIGEMM_FP8_E4M3),
+     migemm.MIGEMM_ERR_UNSUPPORTED),                                        # 192 rows: bf16 only
     (dict(flags=migemm.MIGEMM_F_STREAM_K_FORCE), migemm.MIGEMM_OK),
     (dict(flags=migemm.MIGEMM_F_STREAM_K_FORCE | migemm.MIGEMM_F_TILE_CONSUMER),
      migemm.MIGEMM_ERR_UNSUPPORTED),

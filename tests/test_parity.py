@@ -17,6 +17,9 @@ from tests.helpers import Problem, check_full, codes, workload_reference
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = list(itertools.product(["row", "col"], ["row", "col"]))
+# bf16 plans without the consumer take 256- or 192-row tiles (the plan
+# chooses; these flags force one).
+TILES = {"m256": migemm.MIGEMM_F_TILE_M256, "m192": migemm.MIGEMM_F_TILE_M192}
 
 
 def plan_for(p: Problem, **kw):
@@ -59,23 +62,28 @@ SHAPES_K_ALIGNED = [(1, 1, 8), (17, 33, 8), (64, 64, 64), (255, 257, 136), (256,
                     (257, 255, 264), (300, 520, 520), (513, 129, 1000)]
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", SHAPES_K_ALIGNED)
-def test_shapes_bf16(la, lb, M, N, K):
+def test_shapes_bf16(la, lb, M, N, K, tile):
     g = torch.Generator().manual_seed(M * 7919 + N * 31 + K)
     p = Problem.random(g, M, N, K, la, lb, dist="normal").to_device()
-    D = p.run(plan_for(p))
+    plan = plan_for(p, flags=TILES[tile])
+    assert plan.info.tile_m == int(tile[1:])
+    D = p.run(plan)
     torch.cuda.synchronize()
     r = check_full(p, D)
     assert ok(r), (la, lb, M, N, K, r)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (15, 17, 17), (100, 300, 255), (257, 129, 63)])
-def test_shapes_any_k_mn_contiguous(M, N, K):
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (15, 17, 17), (100, 300, 255), (257, 129, 63),
+                                   (450, 200, 130)])
+def test_shapes_any_k_mn_contiguous(M, N, K, tile):
     """A column-major and B row-major: K needs no alignment."""
     g = torch.Generator().manual_seed(K)
     p = Problem.random(g, M, N, K, "col", "row", dist="normal").to_device()
-    D = p.run(plan_for(p))
+    D = p.run(plan_for(p, flags=TILES[tile]))
     torch.cuda.synchronize()
     assert ok(check_full(p, D))
 
@@ -83,16 +91,17 @@ def test_shapes_any_k_mn_contiguous(M, N, K):
 K_TAIL_LAYOUTS = [("row", "col"), ("row", "row"), ("col", "col")]   # a K-contiguous operand
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("la,lb", K_TAIL_LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(64, 64, 1), (100, 130, 7), (257, 129, 9), (300, 260, 5001),
                                    (520, 264, 71)])
-def test_any_k_with_k_contiguous_operands(la, lb, M, N, K):
+def test_any_k_with_k_contiguous_operands(la, lb, M, N, K, tile):
     """K not a multiple of 8: the last 16-byte chunk of a K-contiguous row
     holds padding past K (NaN here), which the K loop must clear."""
     g = torch.Generator().manual_seed(K * 131 + M)
     p = Problem.random(g, M, N, K, la, lb, dist="normal").poison_padding().to_device()
-    print(f"[parity] any K {M}x{N}x{K} A {la} B {lb}", flush=True)
-    D = p.run(plan_for(p))
+    print(f"[parity] any K {M}x{N}x{K} A {la} B {lb} tile {tile}", flush=True)
+    D = p.run(plan_for(p, flags=TILES[tile]))
     torch.cuda.synchronize()
     r = check_full(p, D)
     assert ok(r), (la, lb, M, N, K, r)
@@ -155,19 +164,23 @@ def test_alpha_beta(alpha, beta):
     (640, 520, 2048, "col", "col"),
 ])
 def test_c_read_schedules_agree(M, N, K, la, lb):
-    """beta != 0: C loaded in the K loop's last two iterations (default) or
-    in the epilogue (MIGEMM_F_C_IN_EPILOGUE) -- the same D bit for bit, and
-    within the bound."""
+    """beta != 0: C loaded in the K loop's last two iterations (the default
+    of 256-row tiles) or in the epilogue (MIGEMM_F_C_IN_EPILOGUE, and 192-row
+    tiles) -- the same D bit for bit, and within the bound."""
     g = torch.Generator().manual_seed(M + K)
     p = Problem.random(g, M, N, K, la, lb, dist="normal", alpha=0.75, beta=-0.5).to_device()
-    plan = plan_for(p)
-    plan_e = plan_for(p, flags=migemm.MIGEMM_F_C_IN_EPILOGUE)
+    m256 = migemm.MIGEMM_F_TILE_M256
+    plan = plan_for(p, flags=m256)
+    plan_e = plan_for(p, flags=m256 | migemm.MIGEMM_F_C_IN_EPILOGUE)
+    plan_s = plan_for(p, flags=migemm.MIGEMM_F_TILE_M192)
     assert plan.info.c_in_k_loop == int(plan.info.num_tiles <= plan.info.grid and K > 64)
-    assert plan_e.info.c_in_k_loop == 0
+    assert plan_e.info.c_in_k_loop == 0 and plan_s.info.c_in_k_loop == 0
     D1 = p.run(plan)
     D2 = p.run(plan_e)
+    D3 = p.run(plan_s)
     torch.cuda.synchronize()
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+    assert torch.equal(D1.view(torch.int16), D3.view(torch.int16))
     assert ok(check_full(p, D1))
 
 
@@ -259,10 +272,14 @@ def test_deterministic_across_runs_and_grid_sizes():
 def test_plan_info_matches_the_persistent_design():
     g = torch.Generator().manual_seed(1)
     p = Problem.random(g, 4000, 3000, 64)
-    info = migemm.Plan(p.desc()).info
+    info = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_M256)).info
     assert (info.tiles_m, info.tiles_n, info.num_tiles) == (16, 12, 192)
     assert info.grid == min(192, info.cu_count)
     assert info.block_threads == 256 and info.tile_m == 256 and info.tile_n == 256
+    # 192 tiles leave a quarter of 256 compute units idle; 192-row tiles fill them
+    short = migemm.Plan(p.desc()).info
+    if info.cu_count >= 252:
+        assert (short.tile_m, short.tiles_m, short.num_tiles, short.grid) == (192, 21, 252, 252)
     assert info.lds_bytes <= 160 * 1024
     props = torch.cuda.get_device_properties(0)
     assert info.cu_count == props.multi_processor_count

@@ -1,7 +1,8 @@
 """Seeded sweep (GPU): random valid combinations of shape, operand layouts,
 element type, alpha/beta, D orientation, batch count, grid cap and mode
 (whole tiles, forced stream-K, tile consumer in either schedule), each checked in full against
-the oracle; the consumer's copy and statistics exactly.  The draws are fixed
+the oracle; the consumer's copy and statistics exactly; bf16 whole tiles
+also under the other tile height (192 or 256 rows), bit for bit.  The draws are fixed
 by the seed, so a failure names a reproducible case."""
 import numpy as np
 import pytest
@@ -47,7 +48,15 @@ def test_sweep(i):
                 beta=c["beta"], d_layout=c["d_layout"])
     p0 = b.p0
     if c["mode"] == "whole":
-        b.check(run(b, migemm.Plan(b.desc(max_workgroups=c["mw"]))))
+        plan = migemm.Plan(b.desc(max_workgroups=c["mw"]))
+        D = run(b, plan)
+        b.check(D)
+        if c["dtype"] == synth.BF16:
+            # the other tile height gives the same bits (each output's sum runs
+            # over K in the same order)
+            other = migemm.MIGEMM_F_TILE_M256 if plan.info.tile_m == 192 else migemm.MIGEMM_F_TILE_M192
+            D2 = run(b, migemm.Plan(b.desc(flags=other, max_workgroups=c["mw"])))
+            assert torch.equal(D.view(torch.int16), D2.view(torch.int16)), "tile heights differ"
     elif c["mode"] == "stream_k":
         plan = migemm.Plan(b.desc(flags=migemm.MIGEMM_F_STREAM_K_FORCE, max_workgroups=c["mw"]))
         ws = None

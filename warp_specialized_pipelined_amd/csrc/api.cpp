@@ -115,8 +115,12 @@ int validate(const migemm_desc* d, Canon* out) {
     return MIGEMM_ERR_UNSUPPORTED;
   constexpr uint32_t kStreamK = MIGEMM_F_STREAM_K | MIGEMM_F_STREAM_K_FORCE;
   if ((d->flags & ~(MIGEMM_F_TILE_CONSUMER | MIGEMM_F_CONSUMER_OVERLAP | MIGEMM_F_HANDOFF_DEBUG |
-                    MIGEMM_F_C_IN_EPILOGUE | kStreamK)) != 0)
+                    MIGEMM_F_C_IN_EPILOGUE | kStreamK | MIGEMM_F_TILE_M256 |
+                    MIGEMM_F_TILE_M192)) != 0)
     return MIGEMM_ERR_INVALID_ARG;
+  if ((d->flags & MIGEMM_F_TILE_M192) &&
+      (d->flags & (MIGEMM_F_TILE_M256 | MIGEMM_F_TILE_CONSUMER | kStreamK)))
+    return MIGEMM_ERR_INVALID_ARG;  // 192-row tiles: whole tiles, no consumer
   if ((d->flags & MIGEMM_F_HANDOFF_DEBUG) && !(d->flags & MIGEMM_F_TILE_CONSUMER))
     return MIGEMM_ERR_INVALID_ARG;
   if (!(d->flags & MIGEMM_F_HANDOFF_DEBUG) && (d->debug_wait_ticks != 0 || d->debug_force_wait != 0))
@@ -131,6 +135,7 @@ int validate(const migemm_desc* d, Canon* out) {
     return MIGEMM_ERR_INVALID_ARG;
   if (d->a_type != d->b_type || d->c_type != MIGEMM_BF16 || d->d_type != MIGEMM_BF16)
     return MIGEMM_ERR_UNSUPPORTED;
+  if ((d->flags & MIGEMM_F_TILE_M192) && es != 2) return MIGEMM_ERR_UNSUPPORTED;
   Orient oa, ob, oc, od;
   if (!orient(d->M, d->K, d->a_rs, d->a_cs, &oa) || !orient(d->K, d->N, d->b_rs, d->b_cs, &ob) ||
       !orient(d->M, d->N, d->c_rs, d->c_cs, &oc) || !orient(d->M, d->N, d->d_rs, d->d_cs, &od))
@@ -221,6 +226,22 @@ bool stream_k_pays(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
   return split < whole;
 }
 
+// The stages one workgroup runs under stream-K (see stream_k_pays).
+int64_t stream_k_stages(int64_t T, int64_t G, int64_t kt, int64_t sk_first) {
+  const int64_t units = (T - sk_first) * kt;
+  return sk_first / G * kt + (units + G - 1) / G + kSkFixupStages;
+}
+
+// Tile height (bf16 whole tiles without the consumer).  A 192-row tile is
+// 3/4 of a 256-row one, so where ceil(T192 / G) * 3/4 < ceil(T256 / G)
+// rounds -- the 256-row tiles fill the last round poorly -- each workgroup
+// has less work with 192.  kShortTileWork is a 192-row tile's time in
+// thousandths of a 256-row one's: 3/4 of the flops at a 6% lower rate per
+// flop (its K loop reads 7 operand fragments from LDS per 12 MFMAs against 8
+// per 16; on MI355X 6144 x 8192 x 8192 in 192-row tiles ran at 1303 TFLOP/s,
+// 8192^3 in 256-row ones at 1384, both four full rounds).
+constexpr int64_t kShortTileWork = 800;
+
 // The plans alive in this process.  Every entry point that takes a plan
 // looks it up here first, so a destroyed plan (or any other pointer that is
 // not a live plan) gives MIGEMM_ERR_INVALID_ARG instead of kernel arguments
@@ -286,6 +307,38 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   p->sel.b_kmajor = !ob.row_major;  // B column-major = K-contiguous
   p->sel.consumer = false;
   p->sel.consumer_overlap = (desc->flags & MIGEMM_F_CONSUMER_OVERLAP) != 0;
+  p->sel.tile_m = migemm::kTileM;
+
+  int grid = p->cu_count;
+  if (desc->max_workgroups > 0 && desc->max_workgroups < grid) grid = desc->max_workgroups;
+  const int64_t kt = (c.K + migemm::kStageKBytes / es - 1) / (migemm::kStageKBytes / es);
+  {
+    // 192-row tiles: forced, or chosen where they leave each workgroup less
+    // work than 256-row tiles (whole, or stream-K where the plan may split).
+    const int64_t tn = (c.N + migemm::kTileN - 1) / migemm::kTileN;
+    const int64_t tm_short = (c.M + migemm::kTileMShort - 1) / migemm::kTileMShort;
+    const bool fits = tm_short < (1 << 20) && (tm_short * tn == 0 ||
+                                               c.L <= (int64_t)0x7FFFFFFF / (tm_short * tn));
+    const uint32_t no_short = MIGEMM_F_TILE_CONSUMER | MIGEMM_F_STREAM_K_FORCE | MIGEMM_F_TILE_M256;
+    if (desc->flags & MIGEMM_F_TILE_M192) {
+      if (!fits) {
+        delete p;
+        return MIGEMM_ERR_UNSUPPORTED;
+      }
+      p->sel.tile_m = migemm::kTileMShort;
+    } else if (es == 2 && !(desc->flags & no_short) && fits && kt > 0 && tm_short * tn > 0) {
+      const int64_t G = grid;
+      const int64_t T = c.L * ((c.M + migemm::kTileM - 1) / migemm::kTileM) * tn;
+      const int64_t T_short = c.L * tm_short * tn;
+      int64_t cost = (T + G - 1) / G * kt * 1000;
+      if (desc->flags & MIGEMM_F_STREAM_K) {
+        const int64_t sk_first = T >= 2 * G ? (T / G - 1) * G : 0;
+        if (stream_k_pays(T, G, kt, sk_first)) cost = stream_k_stages(T, G, kt, sk_first) * 1000;
+      }
+      if ((T_short + G - 1) / G * kt * kShortTileWork < cost) p->sel.tile_m = migemm::kTileMShort;
+    }
+  }
+  const int tile_m = p->sel.tile_m;
 
   KernelArgs& a = p->base;
   a.M = c.M;
@@ -297,7 +350,7 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   a.ldd = c.d_rs;
   a.a_bytes = extent_bytes(c.M, c.K, c.a_rs, c.a_cs, es);
   a.b_bytes = extent_bytes(c.K, c.N, c.b_rs, c.b_cs, es);
-  a.tiles_m = (int32_t)((c.M + migemm::kTileM - 1) / migemm::kTileM);
+  a.tiles_m = (int32_t)((c.M + tile_m - 1) / tile_m);
   a.tiles_n = (int32_t)((c.N + migemm::kTileN - 1) / migemm::kTileN);
   a.tiles_per_batch = a.tiles_m * a.tiles_n;
   a.num_tiles = (int32_t)(c.L * a.tiles_per_batch);
@@ -309,16 +362,13 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   a.c_preload = 0;
   a.stat_ld = a.tiles_n;
 
-  int grid = p->cu_count;
-  if (desc->max_workgroups > 0 && desc->max_workgroups < grid) grid = desc->max_workgroups;
-  const int64_t kt = (c.K + migemm::kStageKBytes / es - 1) / (migemm::kStageKBytes / es);
   a.sk_kt = (int32_t)kt;
   a.sk_first = a.num_tiles;
   // Whole tiles for all but the last round (when there are at least two),
   // then the remaining tiles as K-stage units over the whole grid.
   const int T = a.num_tiles;
   const int sk_first = T >= 2 * grid ? (T / grid - 1) * grid : 0;
-  const bool sk = kt > 0 && T > 0 &&
+  const bool sk = kt > 0 && T > 0 && tile_m == migemm::kTileM &&
                   ((desc->flags & MIGEMM_F_STREAM_K_FORCE) ||
                    ((desc->flags & MIGEMM_F_STREAM_K) && stream_k_pays(T, grid, kt, sk_first)));
   if (sk) {
@@ -341,7 +391,7 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   // 7.9%).  With more rounds the extra loads in iteration KT-2 cost more than
   // they hide (8192^3: 4.8% instead of 2.8%).
   a.c_preload = !(desc->flags & MIGEMM_F_C_IN_EPILOGUE) && !p->sel.stream_k &&
-                a.num_tiles <= grid && kt >= 2;
+                tile_m == migemm::kTileM && a.num_tiles <= grid && kt >= 2;
   if (desc->flags & MIGEMM_F_HANDOFF_DEBUG) {
     p->debug = true;
     p->trace_tiles = grid > 0 ? (a.num_tiles + grid - 1) / grid : 0;
@@ -362,11 +412,12 @@ int gemm_plan_create(const migemm_desc* desc, migemm_plan** out) {
   }
   if (trace_enabled()) {
     std::fprintf(stderr,
-                 "[migemm] plan M=%lld N=%lld K=%lld es=%d A:%s B:%s swapped=%d tiles=%dx%d "
-                 "grid=%d group_m=%d lds=%d stages=%d cus=%d stream_k_tiles=%d workspace=%zu\n",
+                 "[migemm] plan M=%lld N=%lld K=%lld es=%d A:%s B:%s swapped=%d tile=%dx%d "
+                 "tiles=%dx%d grid=%d group_m=%d lds=%d stages=%d cus=%d stream_k_tiles=%d "
+                 "workspace=%zu\n",
                  (long long)c.M, (long long)c.N, (long long)c.K, es,
                  p->sel.a_kmajor ? "K-contig" : "M-contig", p->sel.b_kmajor ? "K-contig" : "N-contig",
-                 (int)c.swapped, a.tiles_m, a.tiles_n, grid, a.group_m,
+                 (int)c.swapped, tile_m, migemm::kTileN, a.tiles_m, a.tiles_n, grid, a.group_m,
                  migemm::kernel_lds_bytes(p->sel), migemm::kStages, p->cu_count,
                  p->sel.stream_k ? a.num_tiles - a.sk_first : 0, p->workspace_bytes);
   }
@@ -398,7 +449,7 @@ int gemm_plan_get_info(const migemm_plan* p, migemm_plan_info* out) {
   out->block_threads = migemm::kThreads;
   out->lds_bytes = migemm::kernel_lds_bytes(p->sel);
   out->stages = migemm::kStages;
-  out->tile_m = migemm::kTileM;
+  out->tile_m = p->sel.tile_m;
   out->tile_n = migemm::kTileN;
   out->tile_k = migemm::kStageKBytes / p->sel.elem_bytes;
   out->swapped = p->swapped ? 1 : 0;

@@ -1,11 +1,13 @@
-// gemm_kernels.hip -- the persistent GEMM kernel and its instantiations.
+// gemm_kernels.hip -- the persistent GEMM kernels and their instantiations.
 //
 // One workgroup of 4 waves per compute unit.  For every tile the scheduler
 // hands it, the workgroup runs the pipelined K loop into a 256 x 256 fp32
 // accumulator tile (128 x 128 per wave) and then the epilogue.  Stream-K
 // kernels then take their range of K-stage units of the remaining tiles
 // (streamk.hpp); tile-consumer kernels pass each finished tile through the
-// hand-off ring to the consumer stage (handoff.hpp).
+// hand-off ring to the consumer stage (handoff.hpp).  A second bf16 kernel
+// takes 192 x 256 tiles, for shapes where 256-row tiles leave compute units
+// idle in the last round.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -158,6 +160,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(KernelArgs a) {
   }
 }
 
+// 192 x 256 tiles (wave tiles of 96 x 128), bf16, whole tiles, no tile
+// consumer.  A problem whose 256 x 256 tiles number a little over a multiple
+// of the grid (192 of them on 256 compute units: a quarter of the units idle)
+// gets 4/3 as many tiles of 3/4 the work; the plan chooses the height that
+// gives each workgroup the least work.  C (beta != 0) is read in the epilogue.
+template <bool AK, bool BK>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel_m192(KernelArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int first = persistent_slot(blockIdx.x, gridDim.x);
+  Accum acc;
+  NoSideWork none;
+  for (int L = first; L < a.num_tiles; L += gridDim.x) {
+    const TileCoord t = tile_of(L, a);
+    const KernelArgs ab = batch_args(a, t.l);
+    const LaneIds id(lane, wave);
+    mainloop<2, AK, BK, 3>(acc, ab, t.tm, t.tn, id.wave, id.lane, none);
+    const LaneIds ie(lane, wave);
+    epilogue_store<3>(acc, ab, t.tm, t.tn, ie.wave, ie.lane);
+    wait_lgkmcnt<0>();  // staging reads done ...
+    barrier();          // ... in every wave before the ring is refilled
+  }
+}
+
 typedef void (*kernel_fn)(KernelArgs);
 
 template <int ES, int CONS, bool SK>
@@ -175,6 +201,10 @@ static kernel_fn pick_mode(const KernelSelect& s) {
 }
 
 static kernel_fn select(const KernelSelect& s) {
+  if (s.tile_m == 192) {
+    if (s.a_kmajor) return s.b_kmajor ? gemm_kernel_m192<true, true> : gemm_kernel_m192<true, false>;
+    return s.b_kmajor ? gemm_kernel_m192<false, true> : gemm_kernel_m192<false, false>;
+  }
   return s.elem_bytes == 2 ? pick_mode<2>(s) : pick_mode<1>(s);
 }
 

@@ -86,11 +86,15 @@ struct CPreload {
 
 // Stage, then store.  The ring must be idle (all waves past the main loop's
 // closing barrier).  Returns with this wave's global stores issued.
-// c_in_lds: C is already in the staging area (CPreload).
+// c_in_lds: C is already in the staging area (CPreload).  BM: the wave's
+// 32-row blocks (4: 256-row tiles; 3: 192-row tiles, whose wave tiles are 96
+// x 128 and use the first 96 rows of the same staging areas).
+template <int BM = 4>
 __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArgs& a, int tm, int tn,
                                                int wave, int lane, bool c_in_lds = false) {
+  constexpr int kRows = 32 * BM;                               // rows of the wave tile
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)tm * kTileM + wm * kWaveTile;   // first row of the wave tile
+  const int64_t m0 = (int64_t)tm * (2 * kRows) + wm * kRows;   // first row of the wave tile
   const int64_t n0 = (int64_t)tn * kTileN + wn * kWaveTile;   // first column
   const int lr = lane & 31;            // row within a 32 x 32 block
   const int half = lane >> 5;          // which 4 of the 8 columns of a chunk
@@ -109,8 +113,11 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
       const uint32_t wave_base = wave * kStagingWaveBytes;
       wait_lgkmcnt<0>();  // earlier reads of this area (the consumer's drain) are done
       static_assert(kStagingWaveBytes % 1024 == 0, "whole LDS-DMA loads per wave");
+      // (96-row wave tiles: the last load also fills 2 staged rows past the
+      // tile's, from C rows that are never stored.)
+      constexpr int kLoads = (kRows * kStagingRowBytes + 1023) / 1024;
 #pragma unroll
-      for (int j = 0; j < kStagingWaveBytes / 1024; ++j) {
+      for (int j = 0; j < kLoads; ++j) {
         const int b = 1024 * j + 16 * lane;
         const int row = b / kStagingRowBytes;
         const int off = b - row * kStagingRowBytes;
@@ -124,7 +131,7 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
     // each read behind the previous chunk's write -- it cannot prove they do
     // not alias -- and every chunk then waits a full LDS round trip.)
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+    for (int bi = 0; bi < BM; ++bi) {
       u32x2 cw[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -147,7 +154,7 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
     }
   } else {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < BM; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
@@ -169,7 +176,7 @@ __device__ __forceinline__ void epilogue_store(const Accum& acc, const KernelArg
   const uint32_t rd_base = wave * kStagingWaveBytes + rsub * kStagingRowBytes + chunk * 16;
   const uint32_t d_lane = (uint32_t)((rsub * a.ldd + 8 * chunk) * 2);
 #pragma unroll 8
-  for (int i = 0; i < kWaveTile / 4; ++i) {
+  for (int i = 0; i < kRows / 4; ++i) {
     const u32x4 v = *(const MIGEMM_LDS u32x4*)lds_at(rd_base + 4 * i * kStagingRowBytes);
     const int row = 4 * i + rsub;
     if (row < rows_left && cols_left > 0) {

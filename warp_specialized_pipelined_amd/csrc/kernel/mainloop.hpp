@@ -167,50 +167,57 @@ struct StageGeom {
 // alone.
 __device__ __forceinline__ int swz_k8(int row) { return (row >> 1) & 7; }
 
-// One operand's share of a wide stage: this wave's 8 LDS-DMA loads of 1 KiB.
-template <int ES, bool KMAJ>
+// One operand's share of a wide stage: this wave's NL LDS-DMA loads of 1 KiB
+// (8: a 256-row operand tile; 6: a 192-row one).  Load idx = NL wave + j of
+// the stage goes to the stage's LDS kilobyte idx.
+template <int ES, bool KMAJ, int NL = 8>
 struct StageLoader {
   typedef StageGeom<ES> G;
+  static_assert(NL == 8 || (NL == 6 && ES == 2), "192-row operand tiles are bf16 only");
   const unsigned char* tile_base;  // operand address of the tile's (row 0, k 0)
   int64_t kstep_bytes;             // address step from one stage of K to the next
   int64_t bytes_left;              // operand bytes from tile_base to its end
-  uint32_t off[8];                 // this lane's byte offset for load j
+  uint32_t off[NL];                // this lane's byte offset for load j
   // The K index (within the stage) that this lane's load j starts at, kept
   // as the two values it takes (K-contiguous: by the parity of j) or as the
-  // value for j = 0 (MN-contiguous: + 8 j), not as 8 registers.
+  // value for j = 0 (MN-contiguous: + 8 j), not as NL registers.  With 6
+  // loads per wave an MN-contiguous operand's panels (8 loads each) start
+  // inside a wave's share: kq[1] is then the wave's first load's position in
+  // its panel.
   int32_t kq[2];
   __device__ __forceinline__ int32_t kpos(int j) const {
     if constexpr (KMAJ) return kq[j & 1];
-    return kq[0] + 8 * j;
+    if constexpr (NL == 8) return kq[0] + 8 * j;
+    return kq[0] + 8 * ((kq[1] + j) & 7);
   }
 
   __device__ __forceinline__ void init(const void* ptr, int64_t bytes, int64_t ld, int64_t origin,
                                        int wave, int lane) {
     const unsigned char* p = static_cast<const unsigned char*>(ptr);
     if constexpr (KMAJ) {
-      // Load idx = 8 wave + j covers rows 8 idx .. 8 idx + 7, 8 lanes a row.
+      // Load idx = NL wave + j covers rows 8 idx .. 8 idx + 7, 8 lanes a row.
       tile_base = p + origin * ld * ES;
       kstep_bytes = kStageKBytes;
       bytes_left = bytes - origin * ld * ES;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = (wave * 8 + j) * 8 + (lane >> 3);
+      for (int j = 0; j < NL; ++j) {
+        const int row = (wave * NL + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz_k8(row);
         off[j] = (uint32_t)(row * ld * ES) + (uint32_t)(c * 16);
       }
       // chunk * elements per chunk for load j: swz_k8 of its row is
-      // 4 (j & 1) + (lane >> 4).
+      // 4 (j & 1) + (lane >> 4) (NL is even).
       kq[0] = ((lane & 7) ^ (lane >> 4)) * G::kElemsPerChunk;
       kq[1] = ((lane & 7) ^ (4 + (lane >> 4))) * G::kElemsPerChunk;
     } else {
-      // Load idx = 8 wave + j fills K rows 8 (idx % L) .. + 7 of panel idx / L
-      // (L loads per panel).
+      // Load idx = NL wave + j fills K rows 8 (idx % L) .. + 7 of panel
+      // idx / L (L loads per panel).
       tile_base = p + origin * ES;
       kstep_bytes = (int64_t)G::kK * ld * ES;
       bytes_left = bytes - origin * ES;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int idx = wave * 8 + j;
+      for (int j = 0; j < NL; ++j) {
+        const int idx = wave * NL + j;
         const int krow = (idx % G::kLoadsPerPanel) * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz_mn<ES>(krow);
         const int col = (idx / G::kLoadsPerPanel) * G::kPanelCols + chunk * G::kElemsPerChunk;
@@ -219,7 +226,7 @@ struct StageLoader {
       // krow of load j is 8 j + (lane >> 3), plus 64 for odd waves when a
       // panel takes 16 loads (e4m3).
       kq[0] = (G::kLoadsPerPanel == 16 ? 64 * (wave & 1) : 0) + (lane >> 3);
-      kq[1] = 0;
+      kq[1] = NL == 8 ? 0 : (wave * NL) & 7;
     }
   }
 
@@ -247,7 +254,7 @@ struct StageLoader {
   template <bool MASK = true>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int krem, uint32_t slot, int wave,
                                        int j) const {
-    dma16(r, lds_at(slot + (wave * 8 + j) * 1024),
+    dma16(r, lds_at(slot + (wave * NL + j) * 1024),
           (!MASK || kpos(j) < krem) ? off[j] : kOobOffset);
   }
   // K-contiguous operands whose K is not a whole number of 16-byte chunks:
@@ -261,10 +268,10 @@ struct StageLoader {
   __device__ __forceinline__ void clear_k_tail(uint32_t slot, int krem, int wave, int lane) const {
     if constexpr (KMAJ) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NL; ++j) {
         const int nb = (krem - kpos(j)) * ES;  // valid bytes of this lane's chunk
         if (nb > 0 && nb < 16) {
-          MIGEMM_LDS u32x4* p = (MIGEMM_LDS u32x4*)lds_at(slot + (wave * 8 + j) * 1024 + 16 * lane);
+          MIGEMM_LDS u32x4* p = (MIGEMM_LDS u32x4*)lds_at(slot + (wave * NL + j) * 1024 + 16 * lane);
           u32x4 x = *p;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
@@ -282,18 +289,18 @@ struct StageLoader {
     int krem;
     const __amdgpu_buffer_rsrc_t r = stage_rsrc(kt, K, &krem);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load(r, krem, slot, wave, j);
+    for (int j = 0; j < NL; ++j) load(r, krem, slot, wave, j);
   }
 };
 
 // Fragment reads from a wide stage: read<BLK, KS> returns the fragment of the
-// wave's 32-row (or -column) block BLK for k-step KS.
-template <int ES, bool KMAJ>
+// wave's 32-row (or -column) block BLK (of NB) for k-step KS.
+template <int ES, bool KMAJ, int NB = 4>
 struct FragReader;
 
 // K-contiguous bf16: one ds_read_b128; k-step ks is chunk 2 ks + (lane / 32).
-template <>
-struct FragReader<2, true> {
+template <int NB>
+struct FragReader<2, true, NB> {
   static constexpr int kReads = 1;
   uint32_t off[4];  // per k-step
   __device__ __forceinline__ void init(int row0, int lane) {
@@ -373,6 +380,41 @@ struct FragReader<2, false> {
   }
 };
 
+// MN-contiguous bf16, the 3 blocks of a wave's 96 rows of a 192-row tile:
+// the same reads, but the second wave's blocks start in the second half of a
+// 64-column panel (rows 96..191 of the tile), so each block has its own lane
+// offset: block b is 32-column half-panel h = col0 / 32 + b, in panel h / 2,
+// on the side h % 2 that the swizzle then flips with k.
+template <>
+struct FragReader<2, false, 3> {
+  typedef StageGeom<2> G;
+  static constexpr int kReads = 2;
+  uint32_t off[3];  // per block
+  __device__ __forceinline__ void init(int col0, int lane) {
+    const int g = lane >> 4, t = lane & 15;
+    const int k = 8 * (g >> 1) + (t >> 2);
+    const int chunk = 2 * (g & 1) + ((t & 3) >> 1);
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const int h = col0 / 32 + b;
+      off[b] = (h >> 1) * G::kPanelBytes + k * kPanelRowBytes +
+               (((4 * (h & 1) + chunk) ^ swz_mn<2>(k)) << 4) + 8 * (t & 1);
+    }
+  }
+  template <int BLK, int KS>
+  __device__ __forceinline__ bf16x8 read(uint32_t opnd_base) const {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    constexpr uint32_t c = 16 * KS * kPanelRowBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK] + c));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MIGEMM_LDS i16x4*)lds_at(opnd_base + off[BLK] + c + 4 * kPanelRowBytes));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
 // MN-contiguous e4m3: four ds_read_b64_tr_b8 per fragment.  Within each
 // group of 16 lanes the instruction reads an 8 x 16 block of bytes (lanes 2r
 // and 2r+1 fetch the two halves of row r) and hands lane i column i, i.e. 8
@@ -409,35 +451,37 @@ struct FragReader<1, false> {
   }
 };
 
-// The fragments of two k-steps (buffer kb holds k-steps of parity kb): 4 A
-// and 4 B fragments each (64 VGPRs for bf16, 128 for e4m3).
-template <int ES, bool AK, bool BK>
+// The fragments of two k-steps (buffer kb holds k-steps of parity kb): BM A
+// and 4 B fragments each (64 VGPRs for bf16 with BM = 4, 128 for e4m3).
+// BM is the wave's count of 32-row blocks: 4 (256-row tiles) or 3 (192).
+template <int ES, bool AK, bool BK, int BM = 4>
 struct Frags {
-  typedef FragReader<ES, AK> RA;
+  typedef FragReader<ES, AK, BM> RA;
   typedef FragReader<ES, BK> RB;
   typedef typename FragType<ES>::type frag_t;
-  static constexpr int kReadInsts = 4 * (RA::kReads + RB::kReads);  // per k-step
-  frag_t a[2][4];
+  static constexpr int kReadInsts = BM * RA::kReads + 4 * RB::kReads;  // per k-step
+  frag_t a[2][BM];
   frag_t b[2][4];
   RA ra;
   RB rb;
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
-    ra.init(wm * kWaveTile, lane);
+    ra.init(wm * 32 * BM, lane);
     rb.init(wn * kWaveTile, lane);
   }
 
-  // Blocks [Q * 4 / NQ, (Q + 1) * 4 / NQ) of k-step KS into buffer KS & 1.
+  // Blocks [Q * 4 / NQ, (Q + 1) * 4 / NQ) of k-step KS into buffer KS & 1
+  // (of A, those below BM).
   template <int KS, int Q, int NQ>
   __device__ __forceinline__ void read_part(uint32_t a_base, uint32_t b_base) {
     static_for<Q * 4 / NQ, (Q + 1) * 4 / NQ>([&](auto xc) {
       constexpr int x = decltype(xc)::value;
-      a[KS & 1][x] = ra.template read<x, KS>(a_base);
+      if constexpr (x < BM) a[KS & 1][x] = ra.template read<x, KS>(a_base);
       b[KS & 1][x] = rb.template read<x, KS>(b_base);
     });
   }
 
-  // MFMAs [FIRST, FIRST + COUNT) of the 16 of buffer KB: MFMA m is block
+  // MFMAs [FIRST, FIRST + COUNT) of the 4 BM of buffer KB: MFMA m is block
   // (m / 4) of A with block (m % 4) of B.
   template <int KB, int FIRST, int COUNT>
   __device__ __forceinline__ void mma(Accum& acc) const {
@@ -470,27 +514,38 @@ struct Frags {
 // path serves the four waves in turn, so loads packed closer than about 64
 // cycles stall the MFMA stream.
 //
+// 192-row tiles (BM = 3, bf16 only): 12 MFMAs per k-step and 6 A loads per
+// wave and stage.  The stage's 8 B loads no longer fit behind every other
+// MFMA of the first k-step: 6 go there, and the last 2 (kBEarly) are issued
+// one stage ahead, in the last k-step of the iteration before (into the
+// slot its barrier frees), behind the MFMAs the A loads leave free.
+//
 // mainloop_range runs K stages [k0, k0 + KT) of the tile (a stream-K
 // segment); K is the problem's K or, for a segment that ends before it, the
 // segment's end: loads past it fall out of range like loads past the
-// problem's K.
-template <int ES, bool AK, bool BK, class SideWork>
+// problem's K.  Only the first BM rows of blocks of acc are used.
+template <int ES, bool AK, bool BK, int BM = 4, class SideWork>
 __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, int tm, int tn,
                                                int wave, int lane, SideWork& side, int k0, int KT,
                                                int64_t K) {
   typedef StageGeom<ES> G;
-  typedef Frags<ES, AK, BK> FW;
+  typedef Frags<ES, AK, BK, BM> FW;
+  static_assert(BM == 4 || (BM == 3 && ES == 2), "192-row tiles are bf16 only");
+  static_assert(BM == 4 || !SideWork::kLoadsC, "C is read in the K loop of 256-row tiles only");
   constexpr bool kBf16 = ES == 2;
   constexpr int kLast = G::kKSteps - 1;
+  constexpr int kM = 4 * BM;                  // MFMAs per k-step
+  constexpr int kBEarly = BM == 4 ? 0 : 2;    // B loads issued one iteration early
+  constexpr int kBLate = 8 - kBEarly;         // B loads in the first k-step
   constexpr uint32_t kB = kOperandStageBytes;
-  StageLoader<ES, AK> la;
+  StageLoader<ES, AK, 2 * BM> la;
   StageLoader<ES, BK> lb;
-  la.init(a.A, a.a_bytes, a.lda, (int64_t)tm * kTileM, wave, lane);
+  la.init(a.A, a.a_bytes, a.lda, (int64_t)tm * (64 * BM), wave, lane);
   lb.init(a.B, a.b_bytes, a.ldb, (int64_t)tn * kTileN, wave, lane);
   const int wm = wave >> 1, wn = wave & 1;
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.v[i][j] = f32x16{};
 
@@ -517,7 +572,14 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     lb.load_all(k0, kB, K, wave);
     la.load_all(k0 + 1, kStageBytes, K, wave);
     if constexpr (kBf16) {
-      wait_vmcnt<8>();
+      if constexpr (kBEarly > 0) {
+        int krem;
+        const __amdgpu_buffer_rsrc_t r = lb.stage_rsrc(k0 + 1, K, &krem);
+        static_for<kBLate, 8>([&](auto jc) {
+          lb.load(r, krem, kStageBytes + kB, wave, decltype(jc)::value);
+        });
+      }
+      wait_vmcnt<2 * BM + kBEarly>();  // stage 0 has landed
     } else {
       lb.load_all(k0 + 1, kStageBytes + kB, K, wave);
       wait_vmcnt<16>();
@@ -548,14 +610,14 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     int krem_a, krem_b;
     const __amdgpu_buffer_rsrc_t ra = la.stage_rsrc(k0 + d + 2, K, &krem_a);
     const __amdgpu_buffer_rsrc_t rb = lb.stage_rsrc(k0 + (kBf16 ? d + 1 : d + 2), K, &krem_b);
-    static_for<0, 16>([&](auto mc) {
+    static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       sched_fence();
       // k-step 1 read one A and one B block at a time, behind every other
       // MFMA (in two bursts of six reads it was 1% slower).
       if constexpr (m % 2 == 0 && m < 8) f.template read_part<1, m / 2, 4>(cur, cur + kB);
       f.template mma<0, m, 1>(acc);
-      if constexpr (kBf16 && (m & 1)) {
+      if constexpr (kBf16 && (m & 1) && (m >> 1) < kBLate) {
         if (!skip_b) lb.template load<kMask>(rb, krem_b, nxt + kB, wave, m >> 1);
       }
     });
@@ -569,7 +631,7 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
         interleave_mfma_reads<4, FW::kReadInsts / 2>();
       });
       sched_fence();
-      f.template mma<ks & 1, 8, 8>(acc);
+      f.template mma<ks & 1, 8, kM - 8>(acc);
     });
     sched_fence();
     // The last k-step's fragments are in registers: this wave is done
@@ -587,7 +649,7 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
     barrier();
     // Anything the side work fetched after the previous barrier has landed.
     side.after_barrier(a, wave, lane);
-    static_for<0, 16>([&](auto mc) {
+    static_for<0, kM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       sched_fence();
       if constexpr (m % 2 == 0 && m >= 2 && m < 10)
@@ -602,6 +664,13 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
         }
       } else if constexpr (kBf16) {
         if constexpr (m & 1) la.template load<kMask>(ra, krem_a, cur, wave, m >> 1);
+        // 192-row tiles: B of stage d+2's last kBEarly loads, into the slot
+        // this iteration's barrier freed, behind MFMAs 0 and 6.
+        if constexpr (kBEarly > 0 && m % 6 == 0) {
+          int krem_b2;
+          const __amdgpu_buffer_rsrc_t rb2 = lb.stage_rsrc(k0 + d + 2, K, &krem_b2);
+          lb.template load<kMask>(rb2, krem_b2, cur + kB, wave, kBLate + m / 6);
+        }
       } else {
         if constexpr (m < 8) la.template load<kMask>(ra, krem_a, cur, wave, m);
         else lb.template load<kMask>(rb, krem_b, cur + kB, wave, m - 8);
@@ -626,8 +695,8 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
   barrier();
 }
 
-// The whole K loop of one output tile.
-template <int ES, bool AK, bool BK, class SideWork>
+// The whole K loop of one output tile (BM: the wave's 32-row blocks).
+template <int ES, bool AK, bool BK, int BM = 4, class SideWork>
 __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm, int tn,
                                          int wave, int lane, SideWork& side) {
   int KT = (int)((a.K + StageGeom<ES>::kK - 1) / StageGeom<ES>::kK);
@@ -635,7 +704,7 @@ __device__ __forceinline__ void mainloop(Accum& acc, const KernelArgs& a, int tm
   // are used, not once before the tile loop and held (or spilled, and
   // reloaded with a vmcnt(0)) across it.
   asm volatile("" : "+s"(KT));
-  mainloop_range<ES, AK, BK>(acc, a, tm, tn, wave, lane, side, 0, KT, a.K);
+  mainloop_range<ES, AK, BK, BM>(acc, a, tm, tn, wave, lane, side, 0, KT, a.K);
 }
 
 }  // namespace migemm

@@ -13,6 +13,9 @@ constexpr int kTileN = 256;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveTile = 128;
+// The other tile height, for bf16 whole tiles without the tile consumer:
+// 192 x 256, wave tiles of 96 x 128 (the plan chooses; gemm_kernel_m192).
+constexpr int kTileMShort = 192;
 // Each stage of the K-loop ring holds 128 bytes of K (64 bf16 or 128 e4m3
 // values) for every row of the A and B tiles: 32 KiB of A + 32 KiB of B.
 // Stage s lives in slot s % kStages of the LDS ring.

@@ -15,6 +15,7 @@ struct KernelSelect {
   bool consumer;    // tile hand-off + consumer stage
   bool consumer_overlap;  // the consumer stage inside the next tile's K loop
   bool stream_k;    // stream-K units after the whole tiles (not with consumer)
+  int tile_m;       // 256, or 192 (bf16 whole tiles without consumer only)
 };
 
 // Dynamic LDS the selected kernel uses.

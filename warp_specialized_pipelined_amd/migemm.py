@@ -33,6 +33,8 @@ MIGEMM_F_STREAM_K_FORCE = 0x4
 MIGEMM_F_HANDOFF_DEBUG = 0x10
 MIGEMM_F_C_IN_EPILOGUE = 0x20
 MIGEMM_F_CONSUMER_OVERLAP = 0x8
+MIGEMM_F_TILE_M256 = 0x40
+MIGEMM_F_TILE_M192 = 0x80
 MIGEMM_TILE_M = 256
 MIGEMM_TILE_N = 256
 
