@@ -14,13 +14,14 @@
 namespace migemm {
 
 // MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
-// and each XCD has its own L2.  Renumber so that the G/8 workgroups resident
-// on one XCD take G/8 consecutive logical slots: at every step they then
-// work on neighbouring tiles of one raster group and share A and B panels in
-// that XCD's L2.
+// and each XCD has its own L2.  Renumber so that the workgroups resident on
+// one XCD take consecutive logical slots: at every step they then work on
+// neighbouring tiles of one raster group and share A and B panels in that
+// XCD's L2.  With G = 8q + r workgroups, XCD x holds q + (x < r) of them
+// (ids x, x + 8, ...), and its slots start after those of XCDs 0 .. x-1.
 __device__ __forceinline__ int persistent_slot(int bid, int grid) {
-  if (grid % 8 != 0) return bid;
-  return (bid % 8) * (grid / 8) + bid / 8;
+  const int q = grid / 8, r = grid % 8, x = bid % 8;
+  return x * q + min(x, r) + bid / 8;
 }
 
 struct TileCoord {
