@@ -83,13 +83,16 @@ def parse():
     ap.add_argument("--settle-seconds", type=float, default=1.5,
                     help="untimed back-to-back steps before the warm-up, for steady clocks")
     ap.add_argument("--variant", choices=["full", "consumer", "overlap", "plain", "fp8", "cfg1", "cfg2",
-                                          "cfg3", "copy", "trace"], default="full",
+                                          "cfg3", "cfg3_m256", "copy", "trace"], default="full",
                     help="profiling runs: time one kernel only and print a short line "
-                         "(copy = a plain 128 MiB device copy, the byte-counter calibration)")
+                         "(copy = a plain 128 MiB device copy, the byte-counter calibration; "
+                         "cfg3_m256 = the ragged workload on 256-row tiles instead of the "
+                         "plan's 192)")
     return ap.parse_args()
 
 
-VARIANTS = {"consumer": 3, "overlap": 3, "plain": 3, "fp8": 4, "cfg1": 0, "cfg2": 1, "cfg3": 2}
+VARIANTS = {"consumer": 3, "overlap": 3, "plain": 3, "fp8": 4, "cfg1": 0, "cfg2": 1, "cfg3": 2,
+            "cfg3_m256": 2}
 
 
 def run_variant(args):
@@ -127,12 +130,14 @@ def run_variant(args):
         fn = lambda: migemm.gemm_run_with_tile_consumer(plan.handle, p.dA, p.dB, None, D, p.alpha,
                                                         0.0, rs, rm, Dc, None, stream)
     else:
-        plan = migemm.Plan(p.desc())
+        flags = migemm.MIGEMM_F_TILE_M256 if args.variant == "cfg3_m256" else 0
+        plan = migemm.Plan(p.desc(flags=flags))
         fn = lambda: migemm.gemm_run(plan.handle, p.dA, p.dB, p.dC, D, p.alpha, p.beta, None,
                                      stream)
     ms = time_calls(fn, args.steps, args.warmup, stream)
     print(json.dumps({"variant": args.variant, "workload": w.name, "ms": round(ms, 4),
-                      "TFLOP/s": round(w.flops / (ms * 1e-3) / 1e12, 1)}))
+                      "TFLOP/s": round(w.flops / (ms * 1e-3) / 1e12, 1),
+                      "tile_m": int(plan.info.tile_m)}))
 
 
 def run_trace(args):
