@@ -76,12 +76,21 @@ def test_d_and_c_beyond_4gib_with_both_consumer_schedules():
     assert M * p.d_rs * 2 > 4 * GiB and M * p.c_rs * 2 > 4 * GiB
     rows, cols = sample_entries(M, N, p.d_rs * 2, 301)
     D = p.new_d()
-    plan = migemm.Plan(p.desc())
+    plan = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_M256))
     print("[max] D, C > 4 GiB: gemm_run", flush=True)
     migemm.gemm_run(plan.handle, p.dA, p.dB, p.dC, D, p.alpha, p.beta)
     torch.cuda.synchronize()
     r = check_sampled(p, D, rows, cols)
     print(f"[max] {r['n']} entries, worst {r['worst_ratio']:.3f}", flush=True)
+
+    # 192-row tiles: D bit for bit as with 256-row ones
+    print("[max] D, C > 4 GiB: gemm_run, 192-row tiles", flush=True)
+    D3 = p.new_d()
+    migemm.gemm_run(migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_M192)), p.dA, p.dB, p.dC, D3,
+                    p.alpha, p.beta)
+    torch.cuda.synchronize()
+    assert torch.equal(D3.view(torch.int16), D.view(torch.int16))
+    del D3
 
     # The tile consumer on the same problem, both schedules: D bit for bit as
     # gemm_run's, the copy bit for bit as D, the statistics of the sampled
@@ -111,9 +120,11 @@ def test_d_and_c_beyond_4gib_with_both_consumer_schedules():
         del D2, Dc, rs, rm
 
 
-def test_k_contiguous_a_beyond_4gib():
+@pytest.mark.parametrize("tile", [migemm.MIGEMM_F_TILE_M256, migemm.MIGEMM_F_TILE_M192],
+                         ids=["m256", "m192"])
+def test_k_contiguous_a_beyond_4gib(tile):
     # Row-major A of 262300 x 8200 bf16 (4.3 GB): the last tile rows start
-    # past 2^32 bytes; ragged M, N and a K tail of 8.
+    # past 2^32 bytes; ragged M, N and a K tail of 8; both tile heights.
     M, N, K = 262300, 200, 8200
     p = big_problem(302, M, N, K, "row", "row").to_device()
     assert M * p.a_rs * 2 > 4 * GiB
@@ -122,8 +133,8 @@ def test_k_contiguous_a_beyond_4gib():
     rows = np.concatenate([rows, np.arange(M - 600, M), np.full(256, (1 << 31) // (K * 2) + 1)])
     cols = np.concatenate([cols, np.arange(600) % N, np.arange(256) % N])
     D = p.new_d()
-    print("[max] K-contiguous A > 4 GiB", flush=True)
-    plan = migemm.Plan(p.desc())
+    print(f"[max] K-contiguous A > 4 GiB, tile flag {tile:#x}", flush=True)
+    plan = migemm.Plan(p.desc(flags=tile))
     migemm.gemm_run(plan, p.dA, p.dB, None, D, p.alpha, 0.0)
     torch.cuda.synchronize()
     check_sampled(p, D, rows, cols)
@@ -140,13 +151,16 @@ def mn_problem():
     del p.dA, p.dB
 
 
-@pytest.mark.parametrize("stream_k", [False, True])
-def test_mn_contiguous_a_beyond_4gib(mn_problem, stream_k):
-    # Whole tiles (64 of them), and stream-K cutting each into K ranges of
-    # four workgroups whose partials meet in the fixup.
+@pytest.mark.parametrize("mode", ["m256", "m192", "stream_k"])
+def test_mn_contiguous_a_beyond_4gib(mn_problem, mode):
+    # Whole tiles (64 of 256 rows, or 86 of 192), and stream-K cutting each
+    # 256-row tile into K ranges of four workgroups whose partials meet in
+    # the fixup.
     p = mn_problem
+    stream_k = mode == "stream_k"
     rows, cols = sample_entries(p.M, p.N, p.d_rs * 2, 303, n_random=768)
-    flags = migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_STREAM_K_FORCE if stream_k else 0
+    flags = {"m256": migemm.MIGEMM_F_TILE_M256, "m192": migemm.MIGEMM_F_TILE_M192,
+             "stream_k": migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_STREAM_K_FORCE}[mode]
     plan = migemm.Plan(p.desc(flags=flags))
     if stream_k:
         assert plan.info.stream_k_tiles == 64
@@ -155,7 +169,7 @@ def test_mn_contiguous_a_beyond_4gib(mn_problem, stream_k):
         ws = torch.empty(plan.workspace_size, dtype=torch.uint8, device="cuda")
         migemm.gemm_workspace_init(plan.handle, ws)
     D = p.new_d()
-    print(f"[max] MN-contiguous A > 4 GiB, stream-K {stream_k}", flush=True)
+    print(f"[max] MN-contiguous A > 4 GiB, {mode}", flush=True)
     migemm.gemm_run(plan.handle, p.dA, p.dB, None, D, p.alpha, 0.0, ws)
     torch.cuda.synchronize()
     check_sampled(p, D, rows, cols)
@@ -183,11 +197,15 @@ def test_batch_strides_beyond_4gib():
     desc = migemm.make_desc(M, N, K, migemm.MIGEMM_BF16, migemm.MIGEMM_BF16, p0.a_rs, p0.a_cs,
                             p0.b_rs, p0.b_cs, p0.c_rs, p0.c_cs, p0.d_rs, p0.d_cs, L=L, a_bs=gap,
                             b_bs=0, c_bs=gap, d_bs=gap)
-    plan = migemm.Plan(desc)
-    migemm.gemm_run(plan.handle, dA, dB, dC, dD, p0.alpha, p0.beta)
-    torch.cuda.synchronize()
-    for l, q in enumerate(ps):
-        Dl = dD[l * gap:l * gap + d_elems].reshape(q.d_shape)
-        ref, absum = q.oracle_full()
-        r = oracle.check(q.d_values(Dl), ref, absum, q.in_dtype(), q.alpha)
-        assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, (l, r)
+    refs = [q.oracle_full() for q in ps]
+    for tile in (migemm.MIGEMM_F_TILE_M256, migemm.MIGEMM_F_TILE_M192):
+        desc.flags = tile
+        plan = migemm.Plan(desc)
+        dD.fill_(float("nan"))
+        migemm.gemm_run(plan.handle, dA, dB, dC, dD, p0.alpha, p0.beta)
+        torch.cuda.synchronize()
+        for l, q in enumerate(ps):
+            Dl = dD[l * gap:l * gap + d_elems].reshape(q.d_shape)
+            ref, absum = refs[l]
+            r = oracle.check(q.d_values(Dl), ref, absum, q.in_dtype(), q.alpha)
+            assert r["n_fail"] == 0 and r["n_nonfinite"] == 0, (tile, l, r)
