@@ -28,9 +28,12 @@ def kernels(tmp_path_factory):
     path = _build.dump_asm(str(tmp_path_factory.mktemp("asm")))
     text = open(path).read()
     out = {}
-    for m in re.finditer(r"^(_ZN6migemm11gemm_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
+    # gemm_kernel<...> and gemm_kernel_m192<...> (mangled with their name lengths, 11 and 16)
+    for m in re.finditer(r"^(_ZN6migemm\d+gemm_kernel\w*?I\S*):[^\n]*\n(.*?)^\.Lfunc_end", text,
+                         re.S | re.M):
         out[m.group(1)] = m.group(2).split("\n")
-    assert len(out) >= 16, "expected the 16 GEMM kernel instantiations"
+    assert len(out) == 36, f"expected the 36 GEMM kernel instantiations, found {len(out)}"
+    assert sum("gemm_kernel_m192" in k for k in out) == 4
     return out
 
 

@@ -77,6 +77,13 @@ def test_bf16_nan_and_infinities_propagate(la, lb):
     print(f"[nonfinite] bf16 {la}/{lb}: {n_nan} NaN, {n_inf} inf, {n_fin} finite outputs", flush=True)
     assert n_nan > 2 * N and n_inf > N
 
+    # The other tile height (192 or 256 rows): the same bits, NaNs included.
+    other = migemm.MIGEMM_F_TILE_M256 if plan.info.tile_m == 192 else migemm.MIGEMM_F_TILE_M192
+    Do = p.new_d()
+    migemm.gemm_run(migemm.Plan(p.desc(flags=other)), p.dA, p.dB, p.dC, Do, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    assert torch.equal(Do.view(torch.int16), D.view(torch.int16))
+
     # Stream-K: the specials meet in partial sums and in the fixup's adds.
     pk = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_STREAM_K | migemm.MIGEMM_F_STREAM_K_FORCE))
     ws = torch.empty(pk.workspace_size, dtype=torch.uint8, device="cuda")

@@ -67,7 +67,7 @@ def bf16_rne_code(x: Fraction) -> int:
     return c | (0x8000 if x < 0 else 0)
 
 
-def run(dtype, A_codes, B_codes, la, lb):
+def run(dtype, A_codes, B_codes, la, lb, flags=0):
     """D = A B with the given element codes, A and B in the given layouts."""
     M, K = A_codes.shape
     N = B_codes.shape[1]
@@ -89,7 +89,7 @@ def run(dtype, A_codes, B_codes, la, lb):
         b_rs, b_cs = 1, K
     else:
         b_rs, b_cs = N, 1
-    desc = migemm.make_desc(M, N, K, t, t, a_rs, a_cs, b_rs, b_cs, N, 1, N, 1)
+    desc = migemm.make_desc(M, N, K, t, t, a_rs, a_cs, b_rs, b_cs, N, 1, N, 1, flags=flags)
     plan = migemm.Plan(desc)
     dA, dB = A.cuda(), B.cuda()
     D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -121,8 +121,10 @@ E4M3_CASES = [
 ]
 
 
+@pytest.mark.parametrize("tile", [migemm.MIGEMM_F_TILE_M256, migemm.MIGEMM_F_TILE_M192],
+                         ids=["m256", "m192"])
 @pytest.mark.parametrize("la,lb", [("row", "row"), ("col", "col"), ("row", "col")])
-def test_bf16_subnormals_are_kept(la, lb):
+def test_bf16_subnormals_are_kept(la, lb, tile):
     M = N = 256
     K = 64
     A = torch.zeros(M, K, dtype=torch.int32)
@@ -135,7 +137,7 @@ def test_bf16_subnormals_are_kept(la, lb):
             B[k, row] = b
             exact += bf16_code_value(a) * bf16_code_value(b)
         want[row] = bf16_rne_code(exact)
-    D = run("bf16", A, B, la, lb)
+    D = run("bf16", A, B, la, lb, tile)
     for row, code in want.items():
         assert int(D[row, row]) == code, (row, hex(int(D[row, row])), hex(code))
     off = D.clone()
