@@ -665,12 +665,16 @@ __device__ __forceinline__ void mainloop_range(Accum& acc, const KernelArgs& a, 
       } else if constexpr (kBf16) {
         if constexpr (m & 1) la.template load<kMask>(ra, krem_a, cur, wave, m >> 1);
         // 192-row tiles: B of stage d+2's last kBEarly loads, into the slot
-        // this iteration's barrier freed, behind MFMAs 0 and 6.
-        if constexpr (kBEarly > 0 && m % 6 == 0) {
-          int krem_b2;
-          const __amdgpu_buffer_rsrc_t rb2 = lb.stage_rsrc(k0 + d + 2, K, &krem_b2);
-          lb.template load<kMask>(rb2, krem_b2, cur + kB, wave, kBLate + m / 6);
-        }
+        // this iteration's barrier freed; early load e behind MFMA e kM /
+        // kBEarly (0 and 6).
+        static_for<0, kBEarly>([&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          if constexpr (e * kM / kBEarly == m) {
+            int krem_b2;
+            const __amdgpu_buffer_rsrc_t rb2 = lb.stage_rsrc(k0 + d + 2, K, &krem_b2);
+            lb.template load<kMask>(rb2, krem_b2, cur + kB, wave, kBLate + e);
+          }
+        });
       } else {
         if constexpr (m < 8) la.template load<kMask>(ra, krem_a, cur, wave, m);
         else lb.template load<kMask>(rb, krem_b, cur + kB, wave, m - 8);
