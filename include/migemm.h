@@ -141,7 +141,11 @@ typedef enum migemm_status {
  *   - each of A, B, C, D has exactly one unit stride, and its other stride
  *     is at least the extent of the contiguous dimension;
  *   - the non-unit stride times the element size is a multiple of 16 bytes
- *     (K itself may be anything, in every layout);
+ *     (K itself may be anything, in every layout); a multiple of 128 bytes
+ *     (64 bf16, 128 e4m3) runs faster: the kernels read 128-byte row
+ *     segments, which then each fall in one cache line (4000 x 3000 x 5000
+ *     bf16 with rows of 10000 and 6000 bytes: 9% slower than with 10112
+ *     and 6144);
  *   - C and D have the same orientation (both row-major or both column-
  *     major); a column-major D is computed as D^T = B^T A^T;
  *   - the tile-consumer flag requires a row-major D;
