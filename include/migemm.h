@@ -188,7 +188,8 @@ typedef struct migemm_plan_info {
   int32_t block_threads;   /* threads per workgroup (4 waves of 64) */
   int32_t lds_bytes;       /* LDS per workgroup (of the kernel gemm_run launches) */
   int32_t stages;          /* depth of the main-loop LDS ring */
-  int32_t tile_m, tile_n, tile_k;
+  int32_t tile_m, tile_n, tile_k; /* output tile (tile_m 256, or 192: MIGEMM_F_TILE_M192) and
+                                      K per pipeline stage (64 bf16, 128 e4m3) */
   int32_t swapped;         /* 1: column-major D, computed as D^T = B^T A^T */
   int32_t a_kmajor;        /* 1: A (after any swap) is K-contiguous */
   int32_t b_kmajor;        /* 1: B (after any swap) is K-contiguous */
