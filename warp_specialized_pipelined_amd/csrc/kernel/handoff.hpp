@@ -6,9 +6,9 @@
 // tile is ready, works on it, and releases the slot -- so that the consumer
 // can run while the MMA warps start the next tile, which a store pipeline
 // drained only at the very end cannot give.  The CUTLASS kernel page starts
-// producers "at the opposite phase" so their first waits pass, and the CuTe
-// DSL pipeline docs name the verbs (producer_acquire / producer_commit /
-// consumer_release).
+// its producers with the phase inverted, so that their first waits pass, and
+// the CuTe DSL pipeline docs name the verbs (producer_acquire /
+// producer_commit / consumer_release).
 //
 // Here the ring lives in LDS: kHandoffSlots slots of
 //     { tile id, full count, empty count }.
