@@ -36,10 +36,21 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "traffic_gemm_consumer_bf16_8192.txt")
 
 
+def code_tokens(text: str) -> str:
+    """C++ source without its comments, and with every run of white space
+    made one space: what the compiler sees, so that an edit to a comment
+    leaves the kernel, and its hash, unchanged.  (String and character
+    literals are kept whole, so a "//" inside one is not a comment.)"""
+    import re
+    pat = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    out = pat.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(out.split())
+
+
 def kernel_source_hash() -> str:
     """sha1 over the device-side sources (the kernel translation unit and its
-    headers), in a fixed order: identifies the kernel whose counters a
-    traffic profile holds."""
+    headers, comments and layout left out), in a fixed order: identifies the
+    kernel whose counters a traffic profile holds."""
     import hashlib
     csrc = os.path.join(HERE, "warp_specialized_pipelined_amd", "csrc")
     files = [os.path.join(csrc, "gemm_kernels.hip"), os.path.join(csrc, "launch.h")]
@@ -48,8 +59,8 @@ def kernel_source_hash() -> str:
     h = hashlib.sha1()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()
 
 

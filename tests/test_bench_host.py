@@ -37,6 +37,28 @@ def test_traffic_is_reported_only_for_the_profiled_kernel(tmp_path, monkeypatch)
     assert bench.measured_traffic() is None
 
 
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    # A copy of the kernel sources: an edited comment or re-spaced line keeps
+    # the hash (the profile still describes the kernel), an edited
+    # statement changes it.
+    import shutil
+    src = os.path.join(ROOT, "warp_specialized_pipelined_amd", "csrc")
+    dst = tmp_path / "warp_specialized_pipelined_amd" / "csrc"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.o", "_build"))
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    assert h0 == (monkeypatch.undo() or bench.kernel_source_hash())   # the copy hashes as the tree
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    f = dst / "kernel" / "params.hpp"
+    text = f.read_text()
+    f.write_text(text.replace("constexpr int kWaves = 4;",
+                              "constexpr   int kWaves = 4;  // four\n/* waves */"))
+    assert bench.kernel_source_hash() == h0
+    f.write_text(text.replace("constexpr int kStages = 2;", "constexpr int kStages = 3;"))
+    assert bench.kernel_source_hash() != h0
+    assert bench.code_tokens('a = "x // y"; // z\nb;') == 'a = "x // y"; b;'
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
