@@ -46,22 +46,26 @@ def replay_and_check(g, outs, want, scribble):
 def test_graph_plain_and_stream_k():
     gen = torch.Generator().manual_seed(11)
     p = Problem.random(gen, 1000, 700, 520, "row", "row", dist="normal", beta=0.5).to_device()
-    plan = migemm.Plan(p.desc())
+    plan = migemm.Plan(p.desc())                                     # 192-row tiles
+    plan_l = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_TILE_M256))   # C read in the K loop
+    assert plan.info.tile_m == 192 and plan_l.info.c_in_k_loop == 1
     sk = migemm.Plan(p.desc(flags=migemm.MIGEMM_F_STREAM_K_FORCE, max_workgroups=6))
     ws = torch.empty(sk.workspace_size, dtype=torch.uint8, device="cuda")
     migemm.gemm_workspace_init(sk.handle, ws)
-    D1, D2 = p.new_d(), p.new_d()
+    D1, D2, D3 = p.new_d(), p.new_d(), p.new_d()
     junk = torch.empty(1 << 20, device="cuda")
 
     def calls(stream):
         migemm.gemm_run(plan.handle, p.dA, p.dB, p.dC, D1, p.alpha, p.beta, None, stream)
         migemm.gemm_run(sk.handle, p.dA, p.dB, p.dC, D2, p.alpha, p.beta, ws, stream)
+        migemm.gemm_run(plan_l.handle, p.dA, p.dB, p.dC, D3, p.alpha, p.beta, None, stream)
 
     calls(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    want = [D1.clone(), D2.clone()]
+    want = [D1.clone(), D2.clone(), D3.clone()]
+    assert torch.equal(want[0].view(torch.int16), want[2].view(torch.int16))
     g = capture(calls)
-    replay_and_check(g, [D1, D2], want, lambda: junk.uniform_())
+    replay_and_check(g, [D1, D2, D3], want, lambda: junk.uniform_())
 
 
 @pytest.mark.parametrize("overlap", [False, True], ids=["staged", "overlap"])
