@@ -8,6 +8,11 @@
  * that are not plans.  Needs no device: validation comes before the device
  * query.  tests/test_abi.py builds and runs it.
  *
+ * The plan flags cycle with the grid (none, each tile height, and flag
+ * combinations that must be refused: 192-row tiles with the tile consumer,
+ * with e4m3 or with both heights); a refused combination that is accepted
+ * fails the run.
+ *
  * Prints the count of descriptions tried and accepted, and exits 0.
  */
 #include <stdint.h>
@@ -35,8 +40,17 @@ static const int64_t kVals[] = {0,
                                 INT64_MAX};
 enum { kNV = sizeof kVals / sizeof kVals[0] };
 
+static const uint32_t kFlags[] = {0,
+                                  MIGEMM_F_TILE_M192,
+                                  MIGEMM_F_TILE_M256,
+                                  MIGEMM_F_TILE_M192 | MIGEMM_F_TILE_CONSUMER,
+                                  MIGEMM_F_TILE_M192 | MIGEMM_F_TILE_M256,
+                                  MIGEMM_F_TILE_CONSUMER | MIGEMM_F_TILE_M256,
+                                  MIGEMM_F_STREAM_K};
+enum { kNF = sizeof kFlags / sizeof kFlags[0] };
+
 int main(void) {
-  long tried = 0, accepted = 0;
+  long tried = 0, accepted = 0, misaccepted = 0;
   for (int dt = 0; dt < 2; ++dt)
     for (int lay = 0; lay < 4; ++lay)
       for (int im = 0; im < kNV; ++im)
@@ -58,8 +72,14 @@ int main(void) {
               for (int b = 0; b < 3; ++b) {
                 d.L = b == 0 ? 1 : (b == 1 ? 3 : INT64_MAX);
                 d.a_bs = d.b_bs = d.c_bs = d.d_bs = b == 0 ? 0 : kVals[(is + 3 * b) % kNV];
+                d.flags = kFlags[(im + in + ik + is + b + lay) % kNF];
                 ++tried;
-                if (gemm_desc_validate(&d) == MIGEMM_OK) ++accepted;
+                if (gemm_desc_validate(&d) == MIGEMM_OK) {
+                  ++accepted;
+                  const int m192 = (d.flags & MIGEMM_F_TILE_M192) != 0;
+                  if (m192 && (dt || (d.flags & (MIGEMM_F_TILE_CONSUMER | MIGEMM_F_TILE_M256))))
+                    ++misaccepted;
+                }
               }
             }
   /* Pointers that are not plans: refused without being read. */
@@ -71,6 +91,10 @@ int main(void) {
       gemm_run(fake, NULL, NULL, NULL, NULL, 1.0f, 0.0f, NULL, NULL) != MIGEMM_ERR_INVALID_ARG ||
       gemm_plan_workspace_size(fake) != 0 || gemm_plan_destroy((migemm_plan*)junk) != MIGEMM_ERR_INVALID_ARG) {
     printf("a pointer that is not a plan was accepted\n");
+    return 1;
+  }
+  if (misaccepted) {
+    printf("%ld refused flag combinations were accepted\n", misaccepted);
     return 1;
   }
   printf("tried %ld accepted %ld\n", tried, accepted);
